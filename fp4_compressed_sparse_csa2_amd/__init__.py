@@ -1,0 +1,21 @@
+"""CSA2 sparse decode over an FP4 E2M1 / E4M3-per-16 global KV cache, native
+to AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libcsa2.so`` (C ABI in
+``include/csa2.h``); this package is its Python binding.  Importing it does
+not load the library; the first call does, and fails loudly if it is missing.
+"""
+from ._lib import (  # noqa: F401
+    PAGE_TOKENS,
+    WINDOW,
+    Cache,
+    Csa2Error,
+    Workspace,
+    index_topk,
+    lib,
+    page_bytes,
+    quantize_append,
+    reindex,
+    sparse_decode,
+    workspace_init,
+)

@@ -1,0 +1,276 @@
+"""ctypes binding of libcsa2.so: argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels; this module
+checks tensor dtypes/devices/shapes, passes ``data_ptr()`` values and the
+current HIP stream, and turns status codes into exceptions.  PyTorch is used
+for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+PAGE_TOKENS = 64
+WINDOW = 128
+
+_c_i32 = ctypes.c_int32
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("pages", _c_vp),
+        ("page_table", _c_vp),
+        ("num_pages", _c_i32),
+        ("max_pages_per_seq", _c_i32),
+        ("batch", _c_i32),
+        ("head_dim", _c_i32),
+        ("idx_dim", _c_i32),
+    ]
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcsa2.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Csa2Error(
+                f"{LIB_PATH} is missing: build it with `python -m fp4_compressed_sparse_csa2_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(CacheStruct)
+        sig = {
+            "csa2_page_bytes": (_c_sz, [_c_i32, _c_i32]),
+            "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "csa2_workspace_init": (ctypes.c_int, [_c_vp, _c_sz, _c_vp]),
+            "csa2_quantize_append": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+            "csa2_index_topk_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32]),
+            "csa2_index_topk": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp,
+                                               _c_vp, _c_vp, _c_sz, _c_vp]),
+            "csa2_reindex_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32]),
+            "csa2_reindex": (ctypes.c_int, [P, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
+                                            _c_vp, _c_vp, _c_sz, _c_vp]),
+            "csa2_sparse_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+            "csa2_sparse_decode": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, ctypes.c_float, _c_vp,
+                                                  _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                                  _c_vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().csa2_status_string(status).decode()
+        raise Csa2Error(f"{what}: {msg} ({status})")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, shape=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _as_u16(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors are passed by their bit patterns."""
+    return t.view(torch.uint16) if t.dtype == torch.bfloat16 else t
+
+
+def page_bytes(head_dim: int, idx_dim: int) -> int:
+    n = lib().csa2_page_bytes(head_dim, idx_dim)
+    if n == 0:
+        raise Csa2Error(f"unsupported head_dim={head_dim} / idx_dim={idx_dim}")
+    return int(n)
+
+
+class Cache:
+    """One owner layer's global state: the page pool and the page table.
+
+    pages       uint8 [num_pages, page_bytes(D, Di)] on the GPU
+    page_table  int32 [batch, max_pages_per_seq] on the same GPU
+    """
+
+    def __init__(self, pages: torch.Tensor, page_table: torch.Tensor, head_dim: int, idx_dim: int):
+        pb = page_bytes(head_dim, idx_dim)
+        _need(pages, "pages", torch.uint8)
+        if pages.dim() != 2 or pages.shape[1] != pb:
+            raise ValueError(f"pages must be [num_pages, {pb}]")
+        _need(page_table, "page_table", torch.int32, pages.device)
+        if page_table.dim() != 2:
+            raise ValueError("page_table must be [batch, max_pages_per_seq]")
+        self.pages, self.page_table = pages, page_table
+        self.head_dim, self.idx_dim = head_dim, idx_dim
+        self.batch, self.max_pages = page_table.shape
+        self.device = pages.device
+        self.struct = CacheStruct(pages.data_ptr(), page_table.data_ptr(), pages.shape[0],
+                                  self.max_pages, self.batch, head_dim, idx_dim)
+
+    @staticmethod
+    def allocate(batch: int, max_pages_per_seq: int, num_pages: int, head_dim: int, idx_dim: int,
+                 page_table: torch.Tensor, device) -> "Cache":
+        pages = torch.zeros((num_pages, page_bytes(head_dim, idx_dim)), dtype=torch.uint8,
+                            device=device)
+        return Cache(pages, page_table.to(device=device, dtype=torch.int32).contiguous(), head_dim,
+                     idx_dim)
+
+
+class Workspace:
+    """A zero-initialised workspace that grows on demand (one per call kind)."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            workspace_init(self.buf)
+        return self.buf
+
+
+def workspace_init(ws: torch.Tensor) -> None:
+    _check(lib().csa2_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream(ws.device)), "csa2_workspace_init")
+
+
+def quantize_append(cache: Cache, x: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                    keys: torch.Tensor | None = None, swa: torch.Tensor | None = None) -> None:
+    """Quantise tokens x (bf16 [n, D]) into the cache at (seq, pos); optional
+    int8 indexer keys [n, Di] and window ring swa (bf16 [B, 128, D])."""
+    x = _as_u16(x)
+    n = x.shape[0]
+    dev = cache.device
+    _need(x, "x", torch.uint16, dev, (n, cache.head_dim))
+    _need(seq, "seq", torch.int32, dev, (n,))
+    _need(pos, "pos", torch.int32, dev, (n,))
+    if keys is not None:
+        _need(keys, "keys", torch.int8, dev, (n, cache.idx_dim))
+    if swa is not None:
+        swa = _as_u16(swa)
+        _need(swa, "swa", torch.uint16, dev, (cache.batch, WINDOW, cache.head_dim))
+    _check(lib().csa2_quantize_append(ctypes.byref(cache.struct), n, x.data_ptr(), _ptr(keys),
+                                      seq.data_ptr(), pos.data_ptr(), _ptr(swa), _stream(dev)),
+           "csa2_quantize_append")
+
+
+def index_topk(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor, K: int,
+               ws: Workspace, out_idx: torch.Tensor | None = None,
+               out_count: torch.Tensor | None = None, out_scores: torch.Tensor | None = None):
+    """Full layer: indexer scores + deterministic Top-K.  Returns (idx [B, K], count [B])."""
+    dev, B = cache.device, cache.batch
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.int32, dev, (B, max_ctx))
+    nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
+    if nbytes == 0:
+        raise Csa2Error(f"index_topk: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_index_topk(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
+                                 q_idx.data_ptr(), K, out_idx.data_ptr(), out_count.data_ptr(),
+                                 _ptr(out_scores), w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_index_topk")
+    return out_idx, out_count
+
+
+def reindex(cache: Cache, q_idx: torch.Tensor, pool: torch.Tensor, pool_count: torch.Tensor,
+            K: int, ws: Workspace, out_idx: torch.Tensor | None = None,
+            out_count: torch.Tensor | None = None, out_scores: torch.Tensor | None = None):
+    """Reindex layer over the owner's pool [B, P].  Returns (idx [B, K], count [B])."""
+    dev, B = cache.device, cache.batch
+    P = pool.shape[1]
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    _need(pool, "pool", torch.int32, dev, (B, P))
+    _need(pool_count, "pool_count", torch.int32, dev, (B,))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.int32, dev, (B, P))
+    nbytes = lib().csa2_reindex_workspace_size(B, P, K)
+    if nbytes == 0:
+        raise Csa2Error(f"reindex: unsupported sizes B={B} P={P} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_reindex(ctypes.byref(cache.struct), q_idx.data_ptr(), pool.data_ptr(),
+                              pool_count.data_ptr(), P, K, out_idx.data_ptr(),
+                              out_count.data_ptr(), _ptr(out_scores), w.data_ptr(), w.numel(),
+                              _stream(dev)),
+           "csa2_reindex")
+    return out_idx, out_count
+
+
+def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_scale: float,
+                  idx: torch.Tensor, idx_count: torch.Tensor, swa: torch.Tensor,
+                  ws: Workspace, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Merged sparse attention.  q bf16 [B, H, D]; idx int32 [B, K]; swa bf16
+    [B, 128, D].  Returns (out fp32 [B, H, D], lse fp32 [B, H] or None)."""
+    dev, B, D = cache.device, cache.batch, cache.head_dim
+    q = _as_u16(q)
+    swa = _as_u16(swa)
+    H = q.shape[1]
+    K = idx.shape[1]
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q, "q", torch.uint16, dev, (B, H, D))
+    _need(idx, "idx", torch.int32, dev, (B, K))
+    _need(idx_count, "idx_count", torch.int32, dev, (B,))
+    _need(swa, "swa", torch.uint16, dev, (B, WINDOW, D))
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, (B, H))
+    nbytes = lib().csa2_sparse_decode_workspace_size(B, H, D, K)
+    if nbytes == 0:
+        raise Csa2Error(f"sparse_decode: unsupported sizes B={B} H={H} D={D} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_sparse_decode(ctypes.byref(cache.struct), ctx_len.data_ptr(), H,
+                                    q.data_ptr(), float(softmax_scale), idx.data_ptr(),
+                                    idx_count.data_ptr(), K, swa.data_ptr(), out.data_ptr(),
+                                    _ptr(lse), w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_sparse_decode")
+    return out, lse

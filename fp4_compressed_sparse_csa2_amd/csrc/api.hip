@@ -1,0 +1,160 @@
+// The C ABI (include/csa2.h): host-side argument validation, then kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// reads of device memory on the host.
+#include "csa2.h"
+
+#include "common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+__global__ __launch_bounds__(kBlock) void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail,
+                                                            size_t ntail) {
+  const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (i < ntail) tail[i] = 0;
+}
+
+hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  const size_t work = n16 > ntail ? n16 : ntail;
+  const size_t blocks = (work + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                     static_cast<uint4*>(ws), n16, static_cast<uint8_t*>(ws) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+}  // namespace csa2
+
+using csa2::CacheArgs;
+
+namespace {
+
+bool supported_d(int D) { return D == 128 || D == 256 || D == 512; }
+bool supported_di(int Di) { return Di == 64 || Di == 128; }
+
+// Common cache checks: returns CSA2_OK or an error code.
+int check_cache(const csa2_cache* c) {
+  if (c == nullptr || c->pages == nullptr || c->page_table == nullptr) return CSA2_E_NULL;
+  if (!supported_d(c->head_dim) || !supported_di(c->idx_dim)) return CSA2_E_UNSUPPORTED;
+  if (c->batch < 1 || c->num_pages < 1 || c->max_pages_per_seq < 1) return CSA2_E_SHAPE;
+  if ((int64_t)c->max_pages_per_seq * CSA2_PAGE_TOKENS > (int64_t)1 << 30) return CSA2_E_SHAPE;
+  return CSA2_OK;
+}
+
+CacheArgs args_of(const csa2_cache* c) {
+  return CacheArgs{c->pages, c->page_table, c->num_pages, c->max_pages_per_seq,
+                   c->batch, c->head_dim, c->idx_dim};
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
+
+constexpr int32_t kMaxK = 65536;
+constexpr int32_t kMaxCtx = 1 << 24;
+
+}  // namespace
+
+extern "C" {
+
+size_t csa2_page_bytes(int32_t head_dim, int32_t idx_dim) {
+  if (!supported_d(head_dim) || !supported_di(idx_dim)) return 0;
+  return (size_t)csa2::page_layout(head_dim, idx_dim).page_bytes;
+}
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_E_NULL: return "CSA2_E_NULL: a required pointer is NULL";
+    case CSA2_E_SHAPE: return "CSA2_E_SHAPE: a size or count is out of range";
+    case CSA2_E_UNSUPPORTED: return "CSA2_E_UNSUPPORTED: head_dim/idx_dim/heads not supported";
+    case CSA2_E_WORKSPACE: return "CSA2_E_WORKSPACE: workspace NULL or too small";
+    case CSA2_E_HIP: return "CSA2_E_HIP: a kernel launch failed";
+    default: return "unknown csa2 status";
+  }
+}
+
+int csa2_workspace_init(void* ws, size_t bytes, void* stream) {
+  if (bytes > 0 && ws == nullptr) return CSA2_E_NULL;
+  return status_of(csa2::run_fill_zero(ws, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_quantize_append(const csa2_cache* cache, int32_t n_tokens, const uint16_t* x,
+                         const int8_t* key_i8, const int32_t* seq, const int32_t* pos,
+                         uint16_t* swa, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (n_tokens < 0) return CSA2_E_SHAPE;
+  if (n_tokens > 0 && (x == nullptr || seq == nullptr || pos == nullptr)) return CSA2_E_NULL;
+  return status_of(csa2::run_quantize_append(args_of(cache), n_tokens, x, key_i8, seq, pos, swa,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_index_topk_workspace_size(int32_t batch, int32_t max_ctx, int32_t K) {
+  if (batch < 1 || max_ctx < 0 || max_ctx > kMaxCtx || K < 0 || K > kMaxK) return 0;
+  return csa2::index_topk_ws_bytes(batch, max_ctx, K);
+}
+
+int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                    const int8_t* q_idx, int32_t K, int32_t* out_idx, int32_t* out_count,
+                    int32_t* out_scores, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q_idx == nullptr || out_count == nullptr) return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
+  const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, out_idx,
+                                        out_count, out_scores, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_reindex_workspace_size(int32_t batch, int32_t P, int32_t K) {
+  if (batch < 1 || P < 0 || P > kMaxK || K < 0 || K > P) return 0;
+  return csa2::reindex_ws_bytes(batch, P, K);
+}
+
+int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx, const int32_t* pool,
+                 const int32_t* pool_count, int32_t P, int32_t K, int32_t* out_idx,
+                 int32_t* out_count, int32_t* out_scores, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (q_idx == nullptr || pool_count == nullptr || out_count == nullptr) return CSA2_E_NULL;
+  if ((P > 0 && pool == nullptr) || (K > 0 && out_idx == nullptr)) return CSA2_E_NULL;
+  if (P < 0 || P > kMaxK || K < 0 || K > P) return CSA2_E_SHAPE;
+  const size_t need = csa2::reindex_ws_bytes(cache->batch, P, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_reindex(args_of(cache), q_idx, pool, pool_count, P, K, out_idx,
+                                     out_count, out_scores, ws,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_sparse_decode_workspace_size(int32_t batch, int32_t H, int32_t head_dim, int32_t K) {
+  if (batch < 1 || H < 16 || H > 128 || H % 16 != 0 || !supported_d(head_dim) || K < 0 ||
+      K > kMaxK)
+    return 0;
+  return csa2::sparse_decode_ws_bytes(batch, H, head_dim, K);
+}
+
+int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t H,
+                       const uint16_t* q, float softmax_scale, const int32_t* idx,
+                       const int32_t* idx_count, int32_t K, const uint16_t* swa, float* out,
+                       float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q == nullptr || idx_count == nullptr || swa == nullptr ||
+      out == nullptr)
+    return CSA2_E_NULL;
+  if (K > 0 && idx == nullptr) return CSA2_E_NULL;
+  if (H < 16 || H > 128 || H % 16 != 0) return CSA2_E_UNSUPPORTED;
+  if (K < 0 || K > kMaxK) return CSA2_E_SHAPE;
+  const size_t need = csa2::sparse_decode_ws_bytes(cache->batch, H, cache->head_dim, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_sparse_decode(args_of(cache), ctx_len, H, q, softmax_scale, idx,
+                                           idx_count, K, swa, out, lse, ws,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

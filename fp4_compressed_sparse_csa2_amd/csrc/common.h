@@ -1,0 +1,108 @@
+// Device helpers shared by the CSA2 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kPage = 64;      // token positions per page
+constexpr int kWindow = 128;   // sliding-window tokens per layer
+constexpr int kGroup = 16;     // channels per E4M3 scale
+constexpr int kBlock = 256;    // threads per block for every kernel here
+constexpr int kKeyBias = 1 << 21;  // |score| <= 127*127*128 < 2^21: key = score + 2^21 is 22-bit
+constexpr int kBins = 2048;    // radix digit = 11 bits; two digits cover the 22-bit key
+
+// Byte layout of one page: codes [64][D/2], scales [64][D/16], keys [64][Di].
+struct PageLayout {
+  int scales_off;
+  int keys_off;
+  int page_bytes;
+};
+__host__ __device__ constexpr PageLayout page_layout(int D, int Di) {
+  return PageLayout{kPage * (D / 2), kPage * (D / 2 + D / 16), kPage * (D / 2 + D / 16 + Di)};
+}
+
+// ------------------------------------------------------------------ lanes
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Sum over aligned groups of 4 lanes (quad_perm swaps) and of 8 lanes
+// (row_half_mirror: lane i of each 8-lane half-row reads lane 7-i, which sits
+// in the other quad).
+__device__ __forceinline__ int sum_quad(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  return v;
+}
+__device__ __forceinline__ int sum_oct(int v) {
+  v = sum_quad(v);
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  return v;
+}
+
+// Exclusive prefix sum over a 256-thread block; returns the prefix, sets *total.
+// `scratch` must hold 4 ints of shared memory.  Contains barriers: every thread
+// of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) {
+    int s = scratch[w];
+    base += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// ------------------------------------------------------------------ FP8 / FP4
+// Value of an E4M3 (OCP "FN") byte with the sign bit clear, as float (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e == 0 ? (float)m * (1.0f / 512.0f) : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E4M3 code of q >= 0: nearest value, ties to the even code, saturating at
+// 448 (0x7E).  q = amax/6 is never within a few ulps of an E4M3 midpoint
+// unless it equals it (amax has 8 significant bits, 6*midpoint at most 8), so
+// rounding q from the fp32 quotient is exact.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  if (!(q < 448.0f)) return 0x7Eu;
+  if (q < 0.015625f) {                               // subnormal grid m * 2^-9, m = 0..8
+    return (uint32_t)__builtin_rintf(q * 512.0f);    // exact scaling, RNE; 8 = 0x08 = 2^-6
+  }
+  uint32_t u = __float_as_uint(q);
+  uint32_t e = ((u >> 23) & 0xFFu) - 120u;          // E4M3 exponent field (1..15)
+  uint32_t mant = u & 0x7FFFFFu;
+  uint32_t m3 = mant >> 20, rem = mant & 0xFFFFFu;
+  uint32_t code = (e << 3) | m3;
+  code += (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E2M1 magnitude code of |x| = xa on the grid {0,.5,1,1.5,2,3,4,6} * s,
+// nearest with ties to the even code.  Midpoint k (between codes k and k+1)
+// sends a tie up when k+1 is even.  All midpoints * s are exact in fp32.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float xa, float s) {
+  uint32_t c = 0;
+  c += xa > 0.25f * s;
+  c += xa >= 0.75f * s;
+  c += xa > 1.25f * s;
+  c += xa >= 1.75f * s;
+  c += xa > 2.5f * s;
+  c += xa >= 3.5f * s;
+  c += xa > 5.0f * s;
+  return s > 0.0f ? c : 0u;
+}
+
+}  // namespace csa2

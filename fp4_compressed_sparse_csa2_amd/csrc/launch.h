@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct CacheArgs {
+  void* pages;
+  const int32_t* page_table;
+  int num_pages;
+  int max_pages;
+  int batch;
+  int D;
+  int Di;
+};
+
+hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st);
+
+hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, const int8_t* key,
+                               const int32_t* seq, const int32_t* pos, uint16_t* swa,
+                               hipStream_t st);
+
+size_t index_topk_ws_bytes(int batch, int max_ctx, int K);
+hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
+                          const int8_t* q_idx, int K, int32_t* out_idx, int32_t* out_count,
+                          int32_t* out_scores, void* ws, hipStream_t st);
+
+size_t reindex_ws_bytes(int batch, int P, int K);
+hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* pool,
+                       const int32_t* pool_count, int P, int K, int32_t* out_idx,
+                       int32_t* out_count, int32_t* out_scores, void* ws, hipStream_t st);
+
+size_t sparse_decode_ws_bytes(int batch, int H, int D, int K);
+hipError_t run_sparse_decode(const CacheArgs& c, const int32_t* ctx_len, int H,
+                             const uint16_t* q, float scale, const int32_t* idx,
+                             const int32_t* idx_count, int K, const uint16_t* swa, float* out,
+                             float* lse, void* ws, hipStream_t st);
+
+}  // namespace csa2

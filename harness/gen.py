@@ -33,7 +33,7 @@ WINDOW = 128          # sliding-window length, tokens
 PAGE = 64             # KV rows per page
 
 # tensor ids for the sub-streams
-T_KV, T_KEYS, T_QIDX, T_Q, T_BOOST, T_LENS, T_PERM, T_APPEND_X, T_APPEND_K = range(9)
+T_KV, T_KEYS, T_QIDX, T_Q, T_BOOST, T_LENS, T_PERM, T_APPEND_X, T_APPEND_K, T_SWA = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -179,6 +179,25 @@ def swa_ring(wl: Workload, kv: np.ndarray, L: int) -> np.ndarray:
     lo = max(0, L - WINDOW)
     pos = np.arange(lo, L)
     ring[pos % WINDOW] = kv[lo:L]
+    return ring
+
+
+def layer_ring(wl: Workload, b: int, L: int, layer: int, kv_tail: np.ndarray | None = None) -> np.ndarray:
+    """Window ring of layer ``layer`` for sequence b at length L (uint16 [W, D]).
+
+    Layer 0 (the cache owner) windows the same tokens that were quantised
+    into the FP4 cache: pass their bf16 rows [max(0, L-W), L) as ``kv_tail``.
+    Every other layer keeps its own window state; its tokens are an
+    independent bf16(N(0,1)) draw."""
+    lo = max(0, L - WINDOW)
+    if layer == 0:
+        assert kv_tail is not None and kv_tail.shape[0] == L - lo
+        rows = kv_tail
+    else:
+        x = _rng(wl, T_SWA, layer, b).standard_normal((L - lo) * wl.D, dtype=np.float32)
+        rows = f32_to_bf16_bits(x).reshape(L - lo, wl.D)
+    ring = np.zeros((WINDOW, wl.D), dtype=np.uint16)
+    ring[np.arange(lo, L) % WINDOW] = rows
     return ring
 
 

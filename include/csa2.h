@@ -1,0 +1,238 @@
+/*
+ * csa2.h -- C ABI of the CSA2 sparse-decode library for MI355X (gfx950).
+ *
+ * The decode step of compressed sparse attention over a shared FP4 global KV
+ * cache, in four calls:
+ *
+ *   csa2_quantize_append  write tokens into the FP4 cache (+ indexer keys,
+ *                         + the layer's 128-token window ring)
+ *   csa2_index_topk       Full layer: int8 indexer scores over every cached
+ *                         position outside the window, deterministic Top-K
+ *   csa2_reindex          Reindex layer: rescore the Full layer's candidate
+ *                         pool with this layer's own indexer query, Top-K'
+ *   csa2_sparse_decode    attention of H query heads over the selected FP4
+ *                         rows (dequantised on the fly) merged with the
+ *                         layer's bf16 window; a Reuse layer calls it with
+ *                         the indices of the layer it reuses
+ *
+ * Sources.  Layers are statically Full, Reindex or Reuse and share the main
+ * KV and the indexer keys, reusing Top-K indices across layers; deeper
+ * indexers refilter only the pool built by the first Full layer (neodrop.ai,
+ * "DeepSeek 首次公开 V4.1-Flash 技术报告", section 架构拆解 item 2; zulogic,
+ * "DeepSeek V4 1-Flash 架构拆解", section 3 mode table).  The main KV is FP4
+ * E2M1 with one E4M3 scale per 16 channels (neodrop.ai, same page, 架构拆解
+ * item 3).  Each layer keeps a 128-token sliding window that is merged with
+ * the global cache (infernews.com, "DeepSeek V4.1 Flash 模型架構與推論優化
+ * 技術規格剖析", section 2; zulogic, same page, section 4).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is DEVICE memory unless marked (host).  All
+ *   buffers are owned by the caller; the library allocates nothing, frees
+ *   nothing and keeps no state between calls.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call only enqueues work on it and returns; nothing synchronises.
+ * - Return value: CSA2_OK, or a negative csa2_status for a host-side
+ *   argument error (nothing is enqueued then) or a failed launch.  The
+ *   library never reads device memory on the host, so contract violations
+ *   that live in device data (an index out of range, a bad page id, a
+ *   length beyond the page table) are not reported: the kernels skip such
+ *   entries without touching memory outside the buffers, and results for
+ *   the affected sequence are unspecified.
+ * - Workspaces: calls that need scratch take (ws, ws_bytes), sized by the
+ *   matching *_workspace_size query.  A workspace must be zero-filled once
+ *   before its first use (csa2_workspace_init, or any zeroing allocation);
+ *   every call returns the control words it uses to zero before it
+ *   finishes, so later calls on the same stream need no re-initialisation.
+ *   One workspace serves one kind of call at a time: two calls in flight on
+ *   different streams need two workspaces, and a workspace handed from one
+ *   kind of call to another must be re-initialised.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_PAGE_TOKENS 64   /* token positions per cache page              */
+#define CSA2_WINDOW 128       /* sliding-window length in tokens              */
+#define CSA2_GROUP 16         /* channels per E4M3 scale                      */
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_E_NULL = -1,          /* a required pointer is NULL                    */
+  CSA2_E_SHAPE = -2,         /* a size or count is out of range               */
+  CSA2_E_UNSUPPORTED = -3,   /* head_dim / idx_dim / heads not supported      */
+  CSA2_E_WORKSPACE = -4,     /* workspace NULL or smaller than required       */
+  CSA2_E_HIP = -5            /* a kernel launch failed                        */
+} csa2_status;
+
+/*
+ * One owner ("Full") layer's global state.  All consumer layers read it.
+ *
+ * pages       device, num_pages * csa2_page_bytes(head_dim, idx_dim) bytes.
+ *             Page layout (64 positions each), back to back:
+ *               codes  [64][head_dim/2]   E2M1 codes; channel 2j in the low
+ *                                         nibble of byte j, 2j+1 in the high
+ *               scales [64][head_dim/16]  E4M3 (OCP "FN") scale of channels
+ *                                         16g..16g+15 in byte g
+ *               keys   [64][idx_dim]      int8 indexer keys
+ * page_table  device int32 [batch][max_pages_per_seq]: physical page of
+ *             logical page i of sequence b (position p lives in page
+ *             page_table[b][p/64], row p%64).  Contiguous caches use the
+ *             identity table; the kernels have one code path.
+ * head_dim    D, latent width of one KV row: 128, 256 or 512.
+ * idx_dim     Di, indexer key width: 64 or 128.
+ */
+typedef struct {
+  void* pages;
+  const int32_t* page_table;
+  int32_t num_pages;
+  int32_t max_pages_per_seq;
+  int32_t batch;
+  int32_t head_dim;
+  int32_t idx_dim;
+} csa2_cache;
+
+/* Bytes of one page: 64 * (D/2 + D/16 + Di).  0 for unsupported D/Di. */
+size_t csa2_page_bytes(int32_t head_dim, int32_t idx_dim);
+
+/* Human-readable name of a csa2_status value (static string). */
+const char* csa2_status_string(int status);
+
+/* Zero-fill `bytes` of workspace `ws` on `stream` with a fill kernel (no
+ * memset node, so the call may be captured in a HIP graph). */
+int csa2_workspace_init(void* ws, size_t bytes, void* stream);
+
+/*
+ * csa2_quantize_append -- FP4/E4M3 pack-and-quantise append.
+ * Source: FP4 main KV = E2M1 codes with one E4M3 scale per 16 channels
+ * (neodrop.ai V4.1-Flash report, 架构拆解 item 3); per-layer window of 128
+ * tokens (zulogic "DeepSeek V4 1-Flash 架构拆解", section 4).
+ *
+ * For each token i < n_tokens, with b = seq[i], p = pos[i]:
+ *   - per group of 16 channels: amax = max |x|; scale s = E4M3(amax/6),
+ *     nearest with ties to the even code, saturating at 448; every channel
+ *     gets the E2M1 code nearest to |x|/s (ties to the even code, sign bit
+ *     = sign bit of x, all-zero magnitudes when s = 0);
+ *   - the codes and scales go to row p of sequence b (layout above);
+ *   - key_i8[i] (if key_i8 != NULL) goes to the indexer-key row of p;
+ *   - x[i] (bf16 bits) goes to window slot p % 128 of swa[b] (if swa != NULL).
+ *
+ * x       device uint16 [n_tokens][D], bf16 bit patterns, finite values.
+ * key_i8  device int8 [n_tokens][Di] or NULL.
+ * seq,pos device int32 [n_tokens].  Tokens with b outside [0, batch), p
+ *         outside [0, 64*max_pages_per_seq) or an out-of-range page id are
+ *         skipped.  Two tokens of one call writing the same row or window
+ *         slot race (either may win).
+ * swa     device uint16 [batch][128][D] ring of this layer, or NULL.
+ * Errors: CSA2_E_NULL (cache, pages, page_table, x, seq, pos when
+ *         n_tokens > 0), CSA2_E_UNSUPPORTED (D, Di), CSA2_E_SHAPE
+ *         (n_tokens < 0, batch/num_pages/max_pages_per_seq < 1).
+ */
+int csa2_quantize_append(const csa2_cache* cache, int32_t n_tokens,
+                         const uint16_t* x, const int8_t* key_i8,
+                         const int32_t* seq, const int32_t* pos,
+                         uint16_t* swa, void* stream);
+
+/*
+ * csa2_index_topk -- Full layer: indexer scores and deterministic Top-K.
+ * Source: shared indexer keys and Top-K addressing indices (neodrop.ai
+ * V4.1-Flash report, 架构拆解 item 2); Full = the layer that builds the
+ * indexer state and runs the sparse selection (zulogic, section 3 table).
+ *
+ * For each sequence b with L = ctx_len[b], n = max(0, L - 128) candidates:
+ *   score[p] = sum_d q_idx[b][d] * key[b][p][d]   (int8 x int8 -> int32, exact)
+ *   selected = the first min(K, n) positions p < n in the order
+ *              (score descending, position ascending);
+ *   out_idx[b]   = selected positions in ascending order, then -1 up to K;
+ *   out_count[b] = min(K, n).
+ *
+ * ctx_len     device int32 [batch], 0 <= L <= 64*max_pages_per_seq.
+ * max_ctx     (host) an upper bound of every ctx_len[b]; sizes the grid and
+ *             the workspace.  Lengths above it are clamped to it.
+ * q_idx       device int8 [batch][Di].
+ * K           0 <= K <= 65536.
+ * out_idx     device int32 [batch][K]; out_count device int32 [batch].
+ * out_scores  device int32 [batch][max_ctx] or NULL: when given, receives
+ *             the scores of positions p < n (other entries untouched).
+ * ws          workspace of csa2_index_topk_workspace_size(batch, max_ctx, K).
+ * Errors: CSA2_E_NULL, CSA2_E_UNSUPPORTED (Di), CSA2_E_SHAPE (K, max_ctx,
+ *         batch), CSA2_E_WORKSPACE.
+ */
+size_t csa2_index_topk_workspace_size(int32_t batch, int32_t max_ctx, int32_t K);
+int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                    const int8_t* q_idx, int32_t K,
+                    int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_reindex -- Reindex layer: refilter the owner's candidate pool.
+ * Source: hierarchical sparse indexer, later indexer layers refilter only
+ * inside the pool built by the first Full layer (neodrop.ai V4.1-Flash
+ * report, 架构拆解 item 2); Reindex = reuse the KV, recompute the index /
+ * candidates (zulogic, section 3 table).
+ *
+ * For each sequence b: the first c = pool_count[b] entries of pool[b] are
+ * scored with this layer's q_idx[b] against the SHARED indexer keys; the
+ * first min(K, c) in (score descending, position ascending) order are
+ * written to out_idx[b] in ascending order, padded with -1 to K, and
+ * out_count[b] = min(K, c).
+ *
+ * pool        device int32 [batch][P]: strictly ascending valid positions
+ *             (the form csa2_index_topk returns); c <= P <= 65536.
+ * K           0 <= K <= P.
+ * out_scores  device int32 [batch][P] or NULL: scores of pool entries.
+ * ws          workspace of csa2_reindex_workspace_size(batch, P, K).
+ * Errors: as csa2_index_topk.
+ */
+size_t csa2_reindex_workspace_size(int32_t batch, int32_t P, int32_t K);
+int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx,
+                 const int32_t* pool, const int32_t* pool_count, int32_t P, int32_t K,
+                 int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_sparse_decode -- merged sparse attention of one layer.
+ * Source: the global cache is merged with the window cache before decoding
+ * (infernews.com V4.1 Flash page, section 2); each layer keeps its own
+ * 128-token window (zulogic, section 4); Reuse layers attend with their own
+ * queries over the reused indices (zulogic, section 3 table).
+ *
+ * For each sequence b (L = ctx_len[b], c = idx_count[b]) and head h < H:
+ *   rows  = E2M1(code) * E4M3(scale) of positions idx[b][0..c) (exact), and
+ *           the window positions [max(0, L-128), L) from swa[b][p % 128];
+ *           each row is both key and value;
+ *   l_j   = softmax_scale * <q[b][h], row_j>;
+ *   out[b][h] = sum_j softmax(l)_j row_j   (one softmax over the union);
+ *   lse[b][h] = max l + ln sum exp(l - max l)   (if lse != NULL).
+ * With no rows at all (L = 0): out = 0, lse = -inf.
+ *
+ * q            device uint16 [batch][H][D] bf16 bits, H a multiple of 16,
+ *              16 <= H <= 128.
+ * idx          device int32 [batch][K]: c distinct positions in [0, L-128);
+ *              entries at or beyond the count are ignored.  0 <= K <= 65536.
+ * swa          device uint16 [batch][128][D] bf16 ring of this layer; its
+ *              values must be finite with magnitude <= 65504 (the window rows
+ *              run through fp16 MFMA operands; magnitudes below 2^-14 keep
+ *              fp16 subnormal precision).
+ * out          device float [batch][H][D]; lse device float [batch][H] or NULL.
+ * ws           workspace of csa2_sparse_decode_workspace_size(batch, H, D, K).
+ * Errors: CSA2_E_NULL, CSA2_E_UNSUPPORTED (D, H), CSA2_E_SHAPE (K, batch),
+ *         CSA2_E_WORKSPACE.
+ */
+size_t csa2_sparse_decode_workspace_size(int32_t batch, int32_t H, int32_t head_dim, int32_t K);
+int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t H,
+                       const uint16_t* q, float softmax_scale,
+                       const int32_t* idx, const int32_t* idx_count, int32_t K,
+                       const uint16_t* swa, float* out, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

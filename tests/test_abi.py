@@ -1,0 +1,75 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/csa2.h declares, and its host-side validation rejects bad arguments
+before anything is launched (these calls reach no HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp4_compressed_sparse_csa2_amd as csa2
+    if not os.path.exists(csa2._lib.LIB_PATH):
+        pytest.skip("libcsa2.so not built")
+    return csa2.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_page_bytes_and_strings(L):
+    assert L.csa2_page_bytes(512, 128) == 64 * (256 + 32 + 128)
+    assert L.csa2_page_bytes(128, 64) == 64 * (64 + 8 + 64)
+    assert L.csa2_page_bytes(100, 64) == 0 and L.csa2_page_bytes(512, 96) == 0
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.csa2_status_string(s).startswith(b"CSA2_")
+
+
+def test_workspace_sizes(L):
+    assert L.csa2_index_topk_workspace_size(8, 65536, 2048) > 8 * 65536 * 12
+    assert L.csa2_index_topk_workspace_size(0, 100, 1) == 0
+    assert L.csa2_reindex_workspace_size(8, 8192, 2048) >= 8 * 8192 * 4
+    assert L.csa2_reindex_workspace_size(8, 100, 200) == 0          # K > P
+    assert L.csa2_sparse_decode_workspace_size(8, 64, 512, 2048) > 0
+    assert L.csa2_sparse_decode_workspace_size(8, 24, 512, 2048) == 0   # H not a multiple of 16
+    assert L.csa2_sparse_decode_workspace_size(8, 64, 384, 2048) == 0   # unsupported D
+
+
+def _cache(D=512, Di=128, batch=1, pages=1, table=1):
+    from fp4_compressed_sparse_csa2_amd._lib import CacheStruct
+    return CacheStruct(pages, table, 4, 4, batch, D, Di)
+
+
+def test_validation_codes(L):
+    c = _cache()
+    P = ctypes.byref
+    assert L.csa2_quantize_append(None, 1, 1, None, 1, 1, None, None) == -1
+    assert L.csa2_quantize_append(P(_cache(pages=0)), 1, 1, None, 1, 1, None, None) == -1
+    assert L.csa2_quantize_append(P(_cache(D=384)), 1, 1, None, 1, 1, None, None) == -3
+    assert L.csa2_quantize_append(P(_cache(batch=0)), 1, 1, None, 1, 1, None, None) == -2
+    assert L.csa2_quantize_append(P(c), -1, 1, None, 1, 1, None, None) == -2
+    assert L.csa2_quantize_append(P(c), 1, None, None, 1, 1, None, None) == -1
+    # index_topk: K out of range, workspace missing / too small
+    assert L.csa2_index_topk(P(c), 1, 100, 1, -1, 1, 1, None, 1, 1 << 30, None) == -2
+    assert L.csa2_index_topk(P(c), 1, 100, 1, 8, 1, 1, None, None, 0, None) == -4
+    assert L.csa2_index_topk(P(c), 1, 100, 1, 8, 1, 1, None, 1, 16, None) == -4
+    # reindex: K > P
+    assert L.csa2_reindex(P(c), 1, 1, 1, 10, 20, 1, 1, None, 1, 1 << 30, None) == -2
+    # sparse_decode: H not a multiple of 16, null output
+    assert L.csa2_sparse_decode(P(c), 1, 24, 1, 1.0, 1, 1, 8, 1, 1, None, 1, 1 << 30, None) == -3
+    assert L.csa2_sparse_decode(P(c), 1, 16, 1, 1.0, 1, 1, 8, 1, None, None, 1, 1 << 30, None) == -1

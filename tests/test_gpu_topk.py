@@ -1,0 +1,107 @@
+"""GPU parity of csa2_index_topk against the oracle: int32 scores and Top-K
+indices bit-exact (ties to the lower position), on small shapes and the edge
+cases of the selection (planted ties, all-equal scores, K = 0, K >= number of
+candidates, context shorter than the window, several bitmap segments, paged
+ragged batches).  Full-size workloads are in test_gpu_configs.py."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_compressed_sparse_csa2_amd as csa2
+from harness import gen
+
+from gpu_common import DEV, GpuCache, log, oracle_topk, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gc: GpuCache, q_idx: np.ndarray, K: int, ws=None, max_ctx=None):
+    wl = gc.wl
+    max_ctx = int(gc.lens.max()) if max_ctx is None else max_ctx
+    ws = ws or csa2.Workspace(DEV)
+    scores = torch.full((wl.B, max_ctx), -7, dtype=torch.int32, device=DEV)
+    idx, cnt = csa2.index_topk(gc.cache, gc.ctx, max_ctx, to_dev(q_idx), K, ws,
+                               out_scores=scores)
+    torch.cuda.synchronize()
+    return to_host(idx), to_host(cnt), to_host(scores)
+
+
+def _check(gc: GpuCache, q_idx: np.ndarray, K: int, **kw):
+    idx, cnt, scores = _run(gc, q_idx, K, **kw)
+    for b in range(gc.wl.B):
+        L = int(gc.lens[b])
+        sc, want, wcnt = oracle_topk(gc.keys[b], q_idx[b], L, K)
+        n = sc.size
+        assert np.array_equal(scores[b, :n], sc), f"scores differ, b={b}"
+        assert int(cnt[b]) == wcnt, f"count b={b}: {cnt[b]} vs {wcnt}"
+        assert np.array_equal(idx[b], want), f"indices differ, b={b}"
+    return idx, cnt
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 255, 256, 3967, 3968, 5000])
+def test_tiny_all_K(K):
+    wl = gen.WORKLOADS["tiny"]
+    log(f"topk tiny K={K}")
+    gc = GpuCache(wl)
+    _check(gc, gen.idx_query(wl), K)
+
+
+@pytest.mark.parametrize("L", [0, 1, 127, 128, 129, 130, 191, 200])
+def test_short_contexts(L):
+    wl = gen.WORKLOADS["tiny"].with_(L=L)
+    log(f"topk short L={L}")
+    gc = GpuCache(wl)
+    _check(gc, gen.idx_query(wl), 16)
+
+
+def _tie_keys(mode):
+    def fn(b, k):
+        L = k.shape[0]
+        if mode == "zeros":
+            return np.zeros_like(k)
+        rng = np.random.default_rng(b)
+        for s in rng.integers(0, max(1, L - 128), 40):       # 40 rows copied onto ~1% each
+            k = gen.plant_ties(k, int(s), rng.integers(0, max(1, L - 128), max(1, L // 100)))
+        return k
+    return fn
+
+
+@pytest.mark.parametrize("mode", ["planted", "zeros"])
+def test_ties_go_to_lower_positions(mode):
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=6000)
+    log(f"topk ties mode={mode}")
+    gc = GpuCache(wl, keys_fn=_tie_keys(mode))
+    q = gen.idx_query(wl)
+    for K in (1, 100, 777, 2048):
+        _check(gc, q, K)
+
+
+def test_several_bitmap_segments_and_large_K():
+    wl = gen.WORKLOADS["tiny"].with_(L=150_000, Di=64)
+    log("topk L=150000 (3 bitmap segments)")
+    gc = GpuCache(wl, keep_kv=False)
+    q = gen.idx_query(wl)
+    for K in (2048, 65536):
+        _check(gc, q, K)
+
+
+def test_paged_ragged_batch_di128():
+    wl = gen.WORKLOADS["b128_rag"].with_(B=16, L=20000, L_min=1, D=128, H=16)
+    log("topk paged ragged B=16")
+    gc = GpuCache(wl)
+    _check(gc, gen.idx_query(wl), 512)
+
+
+def test_deterministic_and_workspace_reuse():
+    """Same call twice on one workspace (the first leaves its control words
+    zero) and on a fresh one: identical bits; a shorter max_ctx bound too."""
+    wl = gen.WORKLOADS["tiny"].with_(B=3, L=9000)
+    gc = GpuCache(wl)
+    q = gen.idx_query(wl)
+    ws = csa2.Workspace(DEV)
+    a = _run(gc, q, 300, ws=ws)
+    b = _run(gc, q, 300, ws=ws)
+    c = _run(gc, q, 300)
+    for x, y in ((a, b), (a, c)):
+        assert all(np.array_equal(u, v) for u, v in zip(x, y))
+    _check(gc, q, 300, ws=ws)
