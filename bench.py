@@ -1,0 +1,388 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the CSA2 sparse-decode library on one MI355X.
+
+Workload ``b8_64k``: batch 8, each sequence 65,536 cached tokens; one Full
+layer with 64 query heads over one latent KV of width 512 stored as FP4 E2M1
+with one E4M3 scale per 16 channels (288 B per token), int8 indexer keys of
+width 128, Top-K 2048 over the positions outside the 128-token window, and a
+bf16 window ring of 128 tokens.  Inputs are seeded synthetic draws (bf16
+N(0,1) latent rows, int8 U{-127..127} keys and indexer query, bf16
+N(0,1)/sqrt(512) queries, softmax scale 1/sqrt(512)).
+
+One step = one decode step of every sequence at this layer, all in the
+library's HIP kernels, on one stream:
+
+  csa2_quantize_append  the step's new token (position L-1) into the FP4 page,
+                        the indexer keys and the window ring
+  csa2_index_topk       int8 scores over the 65,408 candidates, Top-2048
+  csa2_sparse_decode    64 heads over 2048 FP4 rows + 128 window rows
+
+Re-appending token L-1 rewrites identical bytes, so every step sees the same
+cache.  A query is one sequence's new token at this layer (all heads); the
+metric is queries per second over the whole job, and the achieved HBM rate
+is the algorithmic bytes of a step (what the method must move: keys, the
+selected rows, the window, queries, outputs) divided by its time.
+
+Timing.  Inputs are resident in HBM before the timed region.  The caches are
+replicated and the steps rotate over the replicas so that no step finds its
+keys in the 256 MB last-level cache.  Steps are captured in HIP graphs
+(torch.cuda.CUDAGraph) and replayed; the timed region is bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on.
+A second timed region replays graphs of one library call at a time to give
+each call's average duration; the dominant call (csa2_index_topk) is priced
+against the HBM roofline.
+
+``cpu_baseline`` times the plain CPU oracle (the checker, not the product) on
+the same seeded workload: whole decode steps of the 8 sequences, repeated
+until about --cpu-seconds of CPU time.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+WORKLOAD = "b8_64k"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse() -> argparse.Namespace:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=5,
+                    help="cache copies the steps rotate over (>= 1 GB in total)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ byte counts
+def algorithmic_bytes(B, L, H, D, Di, K, W=128):
+    """Bytes per step each call must move (per query figures times B)."""
+    R = D // 2 + D // 16
+    n = max(0, L - W)
+    topk = n * Di + Di + 4 * K + 4 * (-(-n // 64)) + 4
+    decode = K * (R + 4) + W * D * 2 + H * D * 2 + H * D * 4 + 4 * H + 4
+    append = (2 * D + Di + 8) + (R + 2 * D + Di)
+    return {"append": B * append, "index_topk": B * topk, "sparse_decode": B * decode}
+
+
+def source_digest() -> str:
+    """Digest of the HIP sources; traffic counters are reused only while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_compressed_sparse_csa2_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU side
+class Setup:
+    def __init__(self, replicas: int):
+        import torch
+
+        import fp4_compressed_sparse_csa2_amd as csa2
+        from harness import gen
+
+        self.torch, self.csa2, self.gen = torch, csa2, gen
+        dev = self.dev = torch.device("cuda:0")
+        wl = self.wl = gen.WORKLOADS[WORKLOAD]
+        B, L, D, Di = wl.B, wl.L, wl.D, wl.Di
+        self.lens = gen.ctx_lens(wl)
+        pt, npages = gen.page_table(wl, self.lens)
+        t0 = time.perf_counter()
+        cache = csa2.Cache.allocate(B, pt.shape[1], npages, D, Di, torch.from_numpy(pt), dev)
+        ring = np.zeros((B, gen.WINDOW, D), np.uint16)
+        self.keys, self.tail = [], []
+        x_new = np.empty((B, D), np.uint16)
+        k_new = np.empty((B, Di), np.int8)
+        for b in range(B):
+            Lb = int(self.lens[b])
+            kv = gen.kv_bf16(wl, b, Lb)
+            keys = gen.idx_keys(wl, b, Lb)
+            csa2.quantize_append(cache, self.t(kv), torch.full((Lb,), b, dtype=torch.int32, device=dev),
+                                 torch.arange(Lb, dtype=torch.int32, device=dev), keys=self.t(keys))
+            ring[b] = gen.swa_ring(wl, kv, Lb)
+            x_new[b], k_new[b] = kv[Lb - 1], keys[Lb - 1]
+            self.keys.append(keys)
+            del kv
+        torch.cuda.synchronize()
+        log(f"cache built: {npages} pages of {cache.pages.shape[1]} B "
+            f"({cache.pages.numel() / 2**20:.0f} MiB) in {time.perf_counter() - t0:.1f} s")
+        self.ring_host = ring
+        self.x_new, self.k_new = x_new, k_new
+        ring_d = self.t(ring)
+        self.caches = [cache] + [csa2.Cache(cache.pages.clone(), cache.page_table, D, Di)
+                                 for _ in range(replicas - 1)]
+        self.rings = [ring_d] + [ring_d.clone() for _ in range(replicas - 1)]
+        self.ctx = self.t(self.lens.astype(np.int32))
+        self.max_ctx = int(self.lens.max())
+        self.q_idx_h, self.q_h = gen.idx_query(wl), gen.query(wl)
+        self.q_idx, self.q = self.t(self.q_idx_h), self.t(self.q_h)
+        self.sigma = float(gen.softmax_scale(wl))
+        self.seq = torch.arange(B, dtype=torch.int32, device=dev)
+        self.pos = self.t((self.lens - 1).astype(np.int32))
+        self.xd, self.kd = self.t(x_new), self.t(k_new)
+        self.idx = torch.empty((B, wl.K), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, wl.H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, wl.H), dtype=torch.float32, device=dev)
+        self.ws_t, self.ws_d = csa2.Workspace(dev), csa2.Workspace(dev)
+        torch.cuda.synchronize()
+
+    def t(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    # the three library calls of one step, on replica r
+    def append(self, r):
+        self.csa2.quantize_append(self.caches[r], self.xd, self.seq, self.pos, keys=self.kd,
+                                  swa=self.rings[r])
+
+    def index_topk(self, r):
+        self.csa2.index_topk(self.caches[r], self.ctx, self.max_ctx, self.q_idx, self.wl.K,
+                             self.ws_t, out_idx=self.idx, out_count=self.cnt)
+
+    def decode(self, r):
+        self.csa2.sparse_decode(self.caches[r], self.ctx, self.q, self.sigma, self.idx, self.cnt,
+                                self.rings[r], self.ws_d, out=self.out, lse=self.lse)
+
+    def step(self, r):
+        self.append(r)
+        self.index_topk(r)
+        self.decode(r)
+
+
+def capture(S: Setup, fn, rs):
+    """HIP graph of fn(r) for r in rs on a side stream (torch's capture stream)."""
+    torch = S.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in rs:
+            fn(r)
+    return g
+
+
+def parity_check(S: Setup) -> str:
+    """Sequences 0 and B-1 of the eager result against the oracle: indices
+    bit-exact, outputs and LSE within 2e-3."""
+    from oracle import attention as OA
+    from oracle import formats as OF
+    from oracle import select as OS
+
+    idx, cnt = S.idx.cpu().numpy(), S.cnt.cpu().numpy()
+    out, lse = S.out.cpu().numpy(), S.lse.cpu().numpy()
+    wl = S.wl
+    worst = 0.0
+    for b in (0, wl.B - 1):
+        L = int(S.lens[b])
+        sc = OS.indexer_scores(S.q_idx_h[b], S.keys[b][:L - 128])
+        want, wc = OS.topk(sc, L, wl.K)
+        assert int(cnt[b]) == wc and np.array_equal(idx[b], want), f"Top-K differs, b={b}"
+        sel = want[:wc]
+        codes, scales = OF.quantize_rows(S.gen.kv_bf16(wl, b, L)[sel])
+        o, l = OA.sparse_decode(S.q_h[b], S.sigma, codes, scales, S.ring_host[b], sel, L)
+        err = max(float(np.max(np.abs(out[b] - o))), float(np.max(np.abs(lse[b] - l))))
+        assert err <= 2e-3, f"attention error {err:.3e}, b={b}"
+        worst = max(worst, err)
+    return f"ok (sequences 0 and {wl.B - 1}: Top-K bit-exact, max-abs error {worst:.1e})"
+
+
+def gpu_bench(args, S: Setup):
+    torch = S.torch
+    R = args.replicas
+    for r in range(R):                       # eager pass: sizes workspaces, checks results
+        S.step(r)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (S.idx, S.cnt, S.out, S.lse)]
+    parity = "skipped" if args.no_parity else parity_check(S)
+    log(f"parity: {parity}")
+
+    per = max(1, 20 // R)                    # replicas x per steps in one graph
+    big = capture(S, S.step, [r for _ in range(per) for r in range(R)])
+    single = [capture(S, S.step, [r]) for r in range(R)]
+    S_big = R * per
+
+    def run_steps(k):
+        for _ in range(k // S_big):
+            big.replay()
+        for j in range(k % S_big):
+            single[j % R].replay()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    for t, r in zip((S.idx, S.cnt, S.out, S.lse), ref):   # replays reproduce the eager result
+        assert torch.equal(t, r), "graph replay differs from the eager step"
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    run_steps(args.steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+
+    # per-call durations: graphs of one call kind over the replicas
+    calls = {}
+    reps = 20
+    for name, fn in (("append", S.append), ("index_topk", S.index_topk),
+                     ("sparse_decode", S.decode)):
+        g = capture(S, fn, [r for _ in range(4) for r in range(R)])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        calls[name] = a.elapsed_time(b) * 1e3 / (reps * 4 * R)      # us per call
+    torch.cuda.synchronize()
+    for t, r in zip((S.idx, S.cnt, S.out, S.lse), ref):
+        assert torch.equal(t, r), "per-call replay differs from the eager step"
+    return wall, ev_ms, calls, parity
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(S: Setup, seconds: float):
+    """The oracle's decode step (append of the new token, indexer scores,
+    Top-K, dequantisation of the selected rows, merged attention) on the same
+    seeded sequences, repeated until ``seconds`` of timed work."""
+    import threadpoolctl
+
+    from oracle import attention as OA
+    from oracle import formats as OF
+    from oracle import select as OS
+
+    wl = S.wl
+    K = wl.K
+    stored = {}                       # the oracle cache's rows at each sequence's selection
+    done, timed = 0, 0.0
+    b = 0
+    while timed < seconds or done < wl.B:
+        L = int(S.lens[b])
+        t0 = time.perf_counter()
+        OF.quantize_rows(S.x_new[b:b + 1])                      # append of the new token
+        sc = OS.indexer_scores(S.q_idx_h[b], S.keys[b][:L - 128])
+        idx, c = OS.topk(sc, L, K)
+        t1 = time.perf_counter()
+        sel = idx[:c]
+        if b not in stored:           # cache content (written at prefill), not part of the step
+            stored[b] = OF.quantize_rows(S.gen.kv_bf16(wl, b, L)[sel])
+        t2 = time.perf_counter()
+        OA.sparse_decode(S.q_h[b], S.sigma, *stored[b], S.ring_host[b], sel, L)
+        t3 = time.perf_counter()
+        timed += (t1 - t0) + (t3 - t2)
+        done += 1
+        b = (b + 1) % wl.B
+    info = threadpoolctl.threadpool_info()
+    threads = max([1] + [int(i.get("num_threads", 1)) for i in info])
+    return {"value": done / timed, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole decode steps (sequences of {WORKLOAD} in turn), "
+                      f"{timed:.1f} s of timed oracle work; numpy float64, BLAS threads {threads}",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+# ------------------------------------------------------------------ main
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by sequence with no communication, so N GPUs "
+              "would each run this same per-GPU workload).", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        return 2
+    S = Setup(args.replicas)
+    wl = S.wl
+    wall, ev_ms, calls, parity = gpu_bench(args, S)
+    B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
+    nbytes = algorithmic_bytes(B, L, H, D, Di, K)
+    step_bytes = sum(nbytes.values())
+    step_s = ev_ms * 1e-3 / args.steps
+    gbs = step_bytes / step_s / 1e9
+    topk_s = calls["index_topk"] * 1e-6
+    topk_gbs = nbytes["index_topk"] / topk_s / 1e9
+    dec_gbs = nbytes["sparse_decode"] / (calls["sparse_decode"] * 1e-6) / 1e9
+    traffic = measured_traffic("index_topk")
+    res = {
+        "metric": "decode attention queries/sec and achieved HBM GB/s (% of peak) at 64K ctx",
+        "value": B * args.steps / wall,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi8->i32 indexer; fp4/bf16->f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded bf16 N(0,1) latent rows, int8 uniform keys)",
+        "config": {"workload": "b8_64k: batch 8, ctx 65536, 64 query heads over one latent-512 "
+                               "FP4 E2M1/E4M3-per-16 KV (288 B/token), int8 indexer dim 128, "
+                               "Top-K 2048 outside the last 128, bf16 SWA 128",
+                   "batch": B, "ctx": L, "heads": H, "head_dim": D, "idx_dim": Di, "top_k": K,
+                   "window": 128, "step": "quantize_append(1 token/seq) + index_topk + sparse_decode",
+                   "replicas": args.replicas, "timing": "HIP graph replays"},
+        "hbm_gbs": gbs,
+        "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
+        "step_bytes": step_bytes,
+        "step_us_events": step_s * 1e6,
+        "calls_us": calls,
+        "calls_gbs": {"index_topk": topk_gbs, "sparse_decode": dec_gbs},
+        "roofline": {"kernel": "csa2_index_topk (index_score_kernel + index_select_kernel)",
+                     "bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": topk_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_us": calls["index_topk"], "bytes_per_launch": nbytes["index_topk"]},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(S, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

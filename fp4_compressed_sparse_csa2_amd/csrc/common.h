@@ -10,7 +10,7 @@ constexpr int kPage = 64;      // token positions per page
 constexpr int kWindow = 128;   // sliding-window tokens per layer
 constexpr int kGroup = 16;     // channels per E4M3 scale
 constexpr int kBlock = 256;    // threads per block for every kernel here
-constexpr int kKeyBias = 1 << 21;  // |score| <= 127*127*128 < 2^21: key = score + 2^21 is 22-bit
+constexpr int kKeyBias = 1 << 21;  // int8 scores at Di <= 128 lie in [-2^21 + 2^14, 2^21]
 constexpr int kBins = 2048;    // radix digit = 11 bits; two digits cover the 22-bit key
 
 // Byte layout of one page: codes [64][D/2], scales [64][D/16], keys [64][Di].
@@ -21,6 +21,15 @@ struct PageLayout {
 };
 __host__ __device__ constexpr PageLayout page_layout(int D, int Di) {
   return PageLayout{kPage * (D / 2), kPage * (D / 2 + D / 16), kPage * (D / 2 + D / 16 + Di)};
+}
+
+// Radix key of an indexer score: score + 2^21 as a 22-bit unsigned number.
+// The one score that reaches 2^21 is (-128)(-128)*128, and no int8 score lies
+// strictly between 2^21 - 128 and 2^21, so folding it onto 2^22 - 1 keeps the
+// order of every pair of distinct scores and every histogram bin below 2048.
+__device__ __forceinline__ uint32_t score_key(int s) {
+  const uint32_t k = (uint32_t)(s + kKeyBias);
+  return k > 0x3FFFFFu ? 0x3FFFFFu : k;
 }
 
 // ------------------------------------------------------------------ lanes

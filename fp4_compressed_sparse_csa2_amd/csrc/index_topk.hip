@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
     const int p = (lp0 + pi) * kPage + ppos;
     if (p < n) {
       sc_row[p] = keep;
-      if (do_hist) atomicAdd(&hist[(uint32_t)(keep + kKeyBias) >> 11], 1u);
+      if (do_hist) atomicAdd(&hist[score_key(keep) >> 11], 1u);
     }
   }
   if (do_hist) {
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void index_select_kernel(
     uint32_t key = 0;
     bool keep = false;
     if (p < n) {
-      key = (uint32_t)(sc_row[p] + kKeyBias);
+      key = score_key(sc_row[p]);
       keep = (key >> 11) >= t1;
       if ((key >> 11) == t1) atomicAdd(&hist2[key & (kBins - 1)], 1u);
     }
@@ -166,10 +166,8 @@ __global__ __launch_bounds__(kBlock) void index_select_kernel(
       uint32_t slot0 = 0;
       if (lane == 0) slot0 = atomicAdd(&cb[kCtrlCandN], (uint32_t)__popcll(m));
       slot0 = (uint32_t)__shfl((int)slot0, 0, 64);
-      if (keep) {
-        const uint32_t r = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        cand_row[slot0 + r] = make_uint2(key, (uint32_t)p);
-      }
+      const uint32_t r = slot0 + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+      if (keep && r < (uint32_t)n) cand_row[r] = make_uint2(key, (uint32_t)p);
     }
   }
   __syncthreads();
@@ -190,8 +188,9 @@ __global__ __launch_bounds__(kBlock) void index_select_kernel(
   find_digit(cb + kCtrlHist2, need1, scan_scratch, &sh_t2, &sh_above2);
   const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
   const int need_ties = need1 - sh_above2;
-  const int n_cand = (int)__hip_atomic_load(&cb[kCtrlCandN], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+  int n_cand = (int)__hip_atomic_load(&cb[kCtrlCandN], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  n_cand = n_cand < n ? n_cand : n;
   const int written = emit_selected(
       [&](int i) { return cand_row[i]; }, n_cand, tau, need_ties, n, sel_bits, tie_bits,
       scan_scratch, [&](int j, int id) { if (j < K) out[j] = id; });

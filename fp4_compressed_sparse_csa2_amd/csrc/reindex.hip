@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
     // an unusable entry (contract violation) ranks below every real score
     const int s = keep_ok ? keep : -kKeyBias;
     sc_row[e] = s;
-    atomicAdd(&hist[(uint32_t)(s + kKeyBias) >> 11], 1u);
+    atomicAdd(&hist[score_key(s) >> 11], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kBins; i += kBlock) {
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
   __syncthreads();
   for (int i = threadIdx.x; i < c; i += kBlock) {
-    const uint32_t key = (uint32_t)(sc_row[i] + kKeyBias);
+    const uint32_t key = score_key(sc_row[i]);
     if ((key >> 11) == t1) atomicAdd(&hist[key & (kBins - 1)], 1u);
   }
   __syncthreads();
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
   const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
   const int need_ties = need1 - sh_above2;
   const int written = emit_selected(
-      [&](int i) { return make_uint2((uint32_t)(sc_row[i] + kKeyBias), (uint32_t)i); }, c, tau,
+      [&](int i) { return make_uint2(score_key(sc_row[i]), (uint32_t)i); }, c, tau,
       need_ties, c, sel_bits, tie_bits, scan_scratch,
       [&](int j, int id) { if (j < K) out[j] = prow[id]; });
   for (int j = written + threadIdx.x; j < K; j += kBlock) out[j] = -1;
