@@ -74,6 +74,12 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="for rocprofv3 --pmc: three 1 GiB device copies (the counter "
+                         "calibration), then --warmup + --steps eager steps; no timing")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the FETCH_SIZE and WRITE_SIZE counter runs of --counter-run "
+                         "into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
@@ -322,9 +328,94 @@ def cpu_baseline(S: Setup, seconds: float):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+# ------------------------------------------------------------------ counters
+CALIB_BYTES = 1 << 30
+STEP_KERNELS = {"index_topk": ("index_score_kernel", "index_select_kernel"),
+                "sparse_decode": ("sparse_decode_kernel", "sparse_combine_kernel"),
+                "append": ("quantize_append_kernel",)}
+
+
+def counter_run(args) -> int:
+    """Device copies of a known size, then eager steps, for the counter passes."""
+    import torch
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
+    bb = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        bb.copy_(a)
+    torch.cuda.synchronize()
+    del a, bb
+    S = Setup(args.replicas)
+    for i in range(args.warmup + args.steps):
+        S.step(i % args.replicas)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": True, "steps": args.steps, "calib_bytes": CALIB_BYTES,
+                      "calib_copies": 3}), flush=True)
+    return 0
+
+
+def _read_counters(d: str, counter: str):
+    """{dispatch id: (kernel name, value)} for one counter from a rocprofv3 --pmc output dir."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (fn, int(row["Dispatch_Id"]))
+                name, val = out.get(key, (row["Kernel_Name"], 0.0))
+                out[key] = (name, val + float(row["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_dir: str, write_dir: str, steps: int) -> dict:
+    """Bytes per launch of each library call from the FETCH_SIZE / WRITE_SIZE
+    passes, each scaled by what the counter reads for a 1 GiB device copy."""
+    res = {"source_digest": source_digest(), "kernels": {}, "calibration": {}}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        recs = _read_counters(d, counter)
+        ordered = [recs[k] for k in sorted(recs, key=lambda k: k[1])]
+        big = [v for n, v in ordered if "copy" in n.lower() and v * 1024 > 0.8 * CALIB_BYTES]
+        if not big:
+            raise SystemExit(f"{counter}: no calibration copy found")
+        calib_kib = float(np.median(big))
+        factor = CALIB_BYTES / (calib_kib * 1024.0)
+        res["calibration"][counter] = {"copy_bytes": CALIB_BYTES, "reads_kib": calib_kib,
+                                       "factor": factor}
+        for call, kernels in STEP_KERNELS.items():
+            tot = 0.0
+            for kname in kernels:
+                vals = [v for n, v in ordered if kname in n][-steps:]
+                if vals:
+                    tot += float(np.mean(vals)) * 1024.0 * factor
+                    per.setdefault(kname, {})[counter] = float(np.mean(vals)) * 1024.0 * factor
+            per.setdefault(call, {})[counter] = tot
+    for name, v in per.items():
+        v["bytes_per_launch"] = v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0)
+        res["kernels"][name] = v
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main() -> int:
     args = parse()
+    if args.traffic_from:
+        rec = traffic_from(*args.traffic_from, args.steps)
+        rec["command"] = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
+                          f"-- python3 bench.py --counter-run --steps {args.steps} "
+                          f"--warmup {args.warmup}")
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step shards by sequence with no communication, so N GPUs "
@@ -334,6 +425,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         return 2
+    if args.counter_run:
+        return counter_run(args)
     S = Setup(args.replicas)
     wl = S.wl
     wall, ev_ms, calls, parity = gpu_bench(args, S)

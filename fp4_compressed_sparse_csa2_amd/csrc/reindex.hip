@@ -32,8 +32,6 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
   constexpr int LPP = DI / 16;
   constexpr int PPL = 64 / LPP;
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sel_bits[kSegWords];
-  __shared__ uint32_t tie_bits[kSegWords];
   __shared__ int scan_scratch[4];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2, sh_last;
 
@@ -125,12 +123,12 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
   find_digit(hist, need1, scan_scratch, &sh_t2, &sh_above2);
   const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
   const int need_ties = need1 - sh_above2;
-  const int written = emit_selected(
-      [&](int i) { return make_uint2(score_key(sc_row[i]), (uint32_t)i); }, c, tau,
-      need_ties, c, sel_bits, tie_bits, scan_scratch,
-      [&](int j, int id) { if (j < K) out[j] = prow[id]; });
+  // the pool is ascending, so pool order is position order
+  const int written = emit_in_order(
+      [&](int i) { return make_uint2(score_key(sc_row[i]), (uint32_t)prow[i]); }, c, tau,
+      need_ties, out, K, scan_scratch);
   for (int j = written + threadIdx.x; j < K; j += kBlock) out[j] = -1;
-  if (threadIdx.x == 0) out_count[b] = written < K ? written : K;
+  if (threadIdx.x == 0) out_count[b] = written;
   for (int i = threadIdx.x; i < kRCtrlWords; i += kBlock) cb[i] = 0u;
 }
 

@@ -8,18 +8,27 @@
 // Reuse layer attends with its own queries over reused indices (same page,
 // section 3).  One latent row per token is both key and value.
 //
-// Block = (sequence, group of 16 heads, token split), 4 waves.  Per 64-token
-// tile:
-//   1. all threads gather/dequantise the tile into LDS as f16 [64][D+8]
-//      (FP4 -> exact E2M1 with the hardware converter at scale 1.0, then an
-//      exact f16 multiply by the E4M3 scale; window rows bf16 -> f16);
+// Work: a sequence's tokens form 64-token tiles -- ceil(K/64) tiles of
+// selected FP4 rows, then two tiles of window rows.  A block owns one
+// (sequence, group of 16 heads) and a run of consecutive tiles (a split);
+// 4 waves.  All splits of one (sequence, head group) land on one XCD.
+//
+// The block starts by loading, all at once, its queries, the indices of its
+// first run of up to 8 tiles and (when it fits in LDS) the sequence's page
+// table; per run it then resolves every row address and keeps the FP4 rows of
+// the next tile in flight (registers) while it computes the current one:
+//   1. dequantise the tile into LDS as f16 [64][D+8] (FP4 -> exact E2M1 with
+//      the hardware converter at scale 1.0, then an exact f16 multiply by the
+//      E4M3 scale; window rows bf16 -> f16, exact);
 //   2. wave w computes S^T = X[16w..16w+16) Q^T with MFMA 16x16x32 f16
 //      (queries pre-scaled per head by a power of two so that their f16 copy
 //      is exact), tile max per head through LDS;
 //   3. online softmax in the exp2 domain, P (f16) to LDS;
 //   4. wave w accumulates O[16 heads][D/4 slice] += P X with MFMA, the X
-//      operand read token-contiguous by ds_read_b64_tr_b16.
-// Splits write (m, l, unnormalised O) and a combine kernel merges them.
+//      operand read token-major by ds_read_b64_tr_b16.
+// A split writes (m, l, unnormalised O); a combine kernel merges the splits
+// of each (sequence, head) by their LSE, every load of a thread in flight at
+// once.
 #include "common.h"
 #include "launch.h"
 
@@ -41,6 +50,10 @@ __device__ __forceinline__ half4 lds_read_tr(const _Float16* p) {
 constexpr int kTile = 64;                  // tokens per tile
 constexpr int kHG = 16;                    // heads per block
 constexpr int kPStride = kTile + 8;        // P tile row stride (halfs)
+constexpr int kRun = 8;                    // tiles whose metadata is loaded together
+constexpr int kWinTiles = kWindow / kTile; // window tiles per sequence
+constexpr int kMaxSplits = 64;
+constexpr int kPtCache = 2048;             // page-table entries cached in LDS (131072 positions)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -75,6 +88,33 @@ __device__ __forceinline__ half8 bf16x8_to_f16(uint4 v) {
   return o;
 }
 
+// One thread's quarter of an FP4 row: D/8 code bytes and D/64 scale bytes.
+template <int D>
+struct RowPart {
+  uint4 c[D / 128];
+  uint2 s;
+};
+
+template <int D>
+__device__ __forceinline__ void load_row_part(RowPart<D>& r, const uint8_t* pages,
+                                              long long rowkey, int page_bytes, int scales_off,
+                                              int g_q) {
+  if (rowkey < 0) return;
+  const uint8_t* page = pages + (size_t)(rowkey >> 6) * page_bytes;
+  const int row = (int)(rowkey & 63);
+  const uint4* cp = reinterpret_cast<const uint4*>(page + row * (D / 2) + g_q * (D / 8));
+#pragma unroll
+  for (int i = 0; i < D / 128; ++i) r.c[i] = cp[i];
+  const uint8_t* sp = page + scales_off + row * (D / 16) + g_q * (D / 64);
+  if constexpr (D == 512) {
+    r.s = *reinterpret_cast<const uint2*>(sp);
+  } else if constexpr (D == 256) {
+    r.s = make_uint2(*reinterpret_cast<const uint32_t*>(sp), 0u);
+  } else {
+    r.s = make_uint2(*reinterpret_cast<const uint16_t*>(sp), 0u);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
@@ -82,7 +122,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, float scale, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ idx_count, int K, const uint16_t* __restrict__ swa,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int batch, int n_splits, int split_tokens) {
+    float2* __restrict__ part_ml, int batch, int n_splits, int split_tiles) {
   constexpr int XS = D + 8;                 // LDS row stride (halfs) of the X tile
   constexpr int KQ = D / 32;                // MFMA k-steps over D for QK
   constexpr int NB = D / 64;                // 16-dim blocks per wave for PV
@@ -92,15 +132,16 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   __shared__ float red_max[4][kHG];
   __shared__ float red_sum[4][kHG];
   __shared__ uint8_t valid[kTile];
+  __shared__ int pt_lds[kPtCache];
 
-  // ---- block -> (sequence, split, head group), head groups of a unit share an XCD
+  // ---- block -> (unit = (sequence, head group), split); a unit's splits share an XCD
   const int n_hg = H / kHG;
-  const int units = batch * n_splits;
-  const int grp = blockIdx.x / (8 * n_hg), rem = blockIdx.x % (8 * n_hg);
-  const int hg = rem / 8;
-  const int unit = grp * 8 + rem % 8;
+  const int units = batch * n_hg;
+  const int xcd = blockIdx.x & 7, r8 = blockIdx.x >> 3;
+  const int unit = xcd + 8 * (r8 / n_splits);
+  const int split = r8 % n_splits;
   if (unit >= units) return;
-  const int b = unit / n_splits, split = unit % n_splits;
+  const int b = unit / n_hg, hg = unit % n_hg;
 
   int L = ctx_len[b];
   L = L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
@@ -108,12 +149,43 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   int cnt = idx_count[b];
   cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
   const int n_win = L < kWindow ? L : kWindow;
-  const int n_tok = cnt + n_win;
-  const int t_begin = split * split_tokens;
-  const int t_end = min(t_begin + split_tokens, n_tok);
+  const int tf_plan = (K + kTile - 1) / kTile;           // FP4 tiles of the plan
+  const int tf = (cnt + kTile - 1) / kTile;              // FP4 tiles holding tokens
+  const int tw = (n_win + kTile - 1) / kTile;            // window tiles holding tokens
+  const int t_begin = split * split_tiles;
+  const int t_end = min(t_begin + split_tiles, tf_plan + kWinTiles);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
+  const int g_tok = tid >> 2;            // gather: token of the tile
+  const int g_q = tid & 3;               // gather: quarter of the channels
+
+  const int32_t* pt = page_table + (size_t)b * max_pages;
+  const int32_t* idx_row = idx + (size_t)b * K;
+  const uint16_t* swa_b = swa + (size_t)b * kWindow * D;
+  const int f_begin = t_begin, f_end = min(t_end, tf);
+
+  // indices of the first run of FP4 tiles
+  int pos[kRun];
+  auto load_pos = [&](int r0) {
+    const int nr = min(kRun, f_end - r0);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const int j = (r0 + i) * kTile + g_tok;
+      pos[i] = (i < nr && j < cnt) ? idx_row[j] : -1;
+    }
+  };
+  if (f_begin < f_end) load_pos(f_begin);
+  // the sequence's page table, into LDS when it fits
+  const bool pt_cached = max_pages <= kPtCache && f_begin < f_end;
+  int ptv[kPtCache / kBlock];
+  if (pt_cached) {
+#pragma unroll
+    for (int i = 0; i < kPtCache / kBlock; ++i) {
+      const int e = i * kBlock + tid;
+      ptv[i] = e < max_pages ? pt[e] : -1;
+    }
+  }
 
   // ---- queries: lane holds head lc, dims 32kk + 8lg .. +8, as exact f16 of q*2^e
   const int head_q = hg * kHG + lc;
@@ -147,6 +219,11 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   }
   // logits in log2 units: scale2 * (q~ . x)
   const float scale2 = ldexpf(scale, -qexp) * kLog2e;
+  if (pt_cached) {
+#pragma unroll
+    for (int i = 0; i < kPtCache / kBlock; ++i) pt_lds[i * kBlock + tid] = ptv[i];
+  }
+  __syncthreads();
 
   // running softmax state: per lane for head lc (QK layout) and for heads
   // 4lg+i (PV layout); identical inputs give identical values in both.
@@ -156,61 +233,9 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* pt = page_table + (size_t)b * max_pages;
-  const int32_t* idx_row = idx + (size_t)b * K;
-  const uint16_t* swa_b = swa + (size_t)b * kWindow * D;
-  const int g_tok = tid >> 2;            // gather: token of the tile
-  const int g_q = tid & 3;               // gather: quarter of the channels
-
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    // ---- 1. gather + dequantise the tile
-    {
-      const int j = t0 + g_tok;
-      _Float16* xrow = X + g_tok * XS + g_q * DQ;
-      bool ok = false;
-      if (j < t_end && j < cnt) {
-        const int p = idx_row[j];
-        const int pg = (p >= 0 && p < n_glob) ? pt[p / kPage] : -1;
-        if (pg >= 0 && pg < num_pages) {
-          ok = true;
-          const uint8_t* page = pages + (size_t)pg * page_bytes;
-          const int r = p % kPage;
-          const uint4* cp = reinterpret_cast<const uint4*>(page + r * (D / 2) + g_q * (DQ / 2));
-          const uint8_t* sp = page + scales_off + r * (D / 16) + g_q * (DQ / 16);
-          uint4 cw[DQ / 32];
-#pragma unroll
-          for (int i = 0; i < DQ / 32; ++i) cw[i] = cp[i];
-          uint8_t sb[DQ / 16];
-#pragma unroll
-          for (int i = 0; i < DQ / 16; ++i) sb[i] = sp[i];
-#pragma unroll
-          for (int g = 0; g < DQ / 16; ++g) {
-            const uint4 c4 = cw[g / 2];
-            const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
-            const uint32_t sc = sb[g];
-            half8 lo, hi;
-            dequant16(w0, w1, sc, lo, hi);
-            *reinterpret_cast<half8*>(xrow + 16 * g) = lo;
-            *reinterpret_cast<half8*>(xrow + 16 * g + 8) = hi;
-          }
-        }
-      } else if (j < t_end) {
-        const int p = L - n_win + (j - cnt);
-        ok = true;
-        const uint4* src =
-            reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + g_q * DQ);
-#pragma unroll
-        for (int i = 0; i < DQ / 8; ++i) *reinterpret_cast<half8*>(xrow + 8 * i) = bf16x8_to_f16(src[i]);
-      }
-      if (!ok) {
-#pragma unroll
-        for (int i = 0; i < DQ / 8; ++i) *reinterpret_cast<half8*>(xrow + 8 * i) = half8{};
-      }
-      if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
-    }
-    __syncthreads();
-
-    // ---- 2. S^T for tokens 16*wave .. +16 of the tile, all 16 heads
+  // ---- compute one tile that sits in X (valid[] marks real tokens)
+  auto compute_tile = [&]() {
+    // S^T for tokens 16*wave .. +16 of the tile, all 16 heads
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
     const _Float16* xa = X + (wave * 16 + lc) * XS + lg * 8;
 #pragma unroll
@@ -230,9 +255,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     if (lg == 0) red_max[wave][lc] = lmax;
     __syncthreads();
 
-    // ---- 3. online softmax
+    // online softmax
     {
-      float mt = fmaxf(fmaxf(red_max[0][lc], red_max[1][lc]), fmaxf(red_max[2][lc], red_max[3][lc]));
+      const float mt =
+          fmaxf(fmaxf(red_max[0][lc], red_max[1][lc]), fmaxf(red_max[2][lc], red_max[3][lc]));
       const float m_new = fmaxf(m_q, mt);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = exp2f(m_q - m_use);
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     }
     __syncthreads();
 
-    // ---- 4. O[16 heads][wave's D/4] += P X
+    // O[16 heads][wave's D/4] += P X
 #pragma unroll
     for (int kb = 0; kb < kTile / 32; ++kb) {
       const half8 a = *reinterpret_cast<const half8*>(Pt + lc * kPStride + kb * 32 + lg * 8);
@@ -280,6 +306,71 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
       }
     }
     __syncthreads();
+  };
+
+  _Float16* xrow = X + g_tok * XS + g_q * DQ;
+
+  // ---- FP4 tiles of this split, in runs of kRun
+  for (int r0 = f_begin; r0 < f_end; r0 += kRun) {
+    const int nr = min(kRun, f_end - r0);
+    if (r0 != f_begin) load_pos(r0);
+    long long rowkey[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const int p = pos[i];
+      const bool in = p >= 0 && p < n_glob;
+      const int pg = !in ? -1 : (pt_cached ? pt_lds[p / kPage] : pt[p / kPage]);
+      rowkey[i] = (pg >= 0 && pg < num_pages) ? ((long long)pg << 6) | (p % kPage) : -1;
+    }
+    RowPart<D> cur, nxt;
+    load_row_part<D>(cur, pages, rowkey[0], page_bytes, scales_off, g_q);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (i >= nr) break;
+      if (i + 1 < nr) load_row_part<D>(nxt, pages, rowkey[i + 1], page_bytes, scales_off, g_q);
+      const bool ok = rowkey[i] >= 0;
+      if (ok) {
+#pragma unroll
+        for (int g = 0; g < DQ / 16; ++g) {
+          const uint4 c4 = cur.c[g / 2];
+          const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
+          const uint32_t sc = ((g < 4 ? cur.s.x : cur.s.y) >> (8 * (g & 3))) & 0xFFu;
+          half8 lo, hi;
+          dequant16(w0, w1, sc, lo, hi);
+          *reinterpret_cast<half8*>(xrow + 16 * g) = lo;
+          *reinterpret_cast<half8*>(xrow + 16 * g + 8) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < DQ / 8; ++k) *reinterpret_cast<half8*>(xrow + 8 * k) = half8{};
+      }
+      if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
+      __syncthreads();
+      compute_tile();
+      cur = nxt;
+    }
+  }
+
+  // ---- window tiles of this split
+  for (int t = max(t_begin, tf_plan); t < t_end; ++t) {
+    const int w = t - tf_plan;
+    if (w >= tw) break;
+    const int k = w * kTile + g_tok;
+    const bool ok = k < n_win;
+    if (ok) {
+      const int p = L - n_win + k;
+      const uint4* src =
+          reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + g_q * DQ);
+#pragma unroll
+      for (int i = 0; i < DQ / 8; ++i)
+        *reinterpret_cast<half8*>(xrow + 8 * i) = bf16x8_to_f16(src[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DQ / 8; ++i) *reinterpret_cast<half8*>(xrow + 8 * i) = half8{};
+    }
+    if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
+    __syncthreads();
+    compute_tile();
   }
 
   // ---- finish: total l per head across waves (every wave saw the same m)
@@ -304,112 +395,164 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
       const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
       lse[(size_t)b * H + hg * kHG + lc] = lt > 0.f ? (m_q + log2f(lt)) * kLn2 : -INFINITY;
     }
-  } else {
-    const size_t pbase = ((size_t)b * n_splits + split) * H;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = hg * kHG + lg * 4 + i;
-      float* orow = part_o + (pbase + head) * D + wave * DQ + lc;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) orow[nb * 16] = acc[nb][i];
-    }
-    if (wave == 0 && lg == 0) {
-      const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
-      part_ml[pbase + hg * kHG + lc] = make_float2(m_q, lt);
-    }
+    return;
   }
+
+  // ---- split partials: (m, l) per head and the unnormalised O
+  const size_t ubase = (size_t)unit * n_splits;          // partial rows of this unit
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = lg * 4 + i;
+    float* orow = part_o + ((ubase + split) * kHG + h) * D + wave * DQ + lc;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) orow[nb * 16] = acc[nb][i];
+  }
+  if (wave == 0 && lg == 0) {
+    const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
+    part_ml[(ubase + split) * kHG + lc] = make_float2(m_q, lt);
+  }
+
 }
 
-// LSE-merge of the split partials: one block per (sequence, head).
-__global__ __launch_bounds__(128) void sparse_combine_kernel(const float* __restrict__ part_o,
-                                                             const float2* __restrict__ part_ml,
-                                                             int H, int D, int n_splits,
-                                                             float* __restrict__ out,
-                                                             float* __restrict__ lse) {
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[((size_t)b * n_splits + s) * H + h].x);
-  const float Mu = M == -INFINITY ? 0.0f : M;
-  float Lsum = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float2 ml = part_ml[((size_t)b * n_splits + s) * H + h];
-    Lsum += ml.y > 0.f ? exp2f(ml.x - Mu) * ml.y : 0.f;
-  }
-  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t r = ((size_t)b * n_splits + s) * H + h;
-      const float2 ml = part_ml[r];
-      if (ml.y > 0.f) acc += exp2f(ml.x - Mu) * part_o[r * D + d];
+// LSE merge of the split partials.  Block = (unit, HPB heads); thread = one
+// float4 of one head's output; every load of a batch of 16 splits is issued
+// before any is used.
+template <int D>
+__global__ __launch_bounds__(kBlock) void sparse_combine_kernel(
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml, int H, int n_splits,
+    float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int T4 = D / 4;                 // threads per head
+  constexpr int HPB = kBlock / T4;          // heads per block
+  constexpr int SB = 16;                    // splits per batch of loads
+  const int n_hg = H / kHG;
+  const int unit = blockIdx.x / (kHG / HPB);
+  const int h = (blockIdx.x % (kHG / HPB)) * HPB + (int)threadIdx.x / T4;
+  const int d4 = (int)threadIdx.x % T4;
+  const int b = unit / n_hg, hg = unit % n_hg;
+  const size_t ubase = (size_t)unit * n_splits;
+  const size_t ostep = (size_t)kHG * D / 4;             // float4s from one split to the next
+  const float4* src = reinterpret_cast<const float4*>(part_o + (ubase * kHG + h) * D) + d4;
+
+  float M = -INFINITY, Lsum = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < n_splits; s0 += SB) {
+    float2 ml[SB];
+    float4 x[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      if (s0 + i < n_splits) {
+        ml[i] = part_ml[(ubase + s0 + i) * kHG + h];
+        x[i] = src[(s0 + i) * ostep];
+      } else {
+        ml[i] = make_float2(-INFINITY, 0.f);
+        x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    out[((size_t)b * H + h) * D + d] = acc * inv;
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      if (ml[i].y > 0.f) mb = fmaxf(mb, ml[i].x);
+    if (mb == -INFINITY) continue;                      // nothing with weight yet
+    const float r = M == -INFINITY ? 0.f : exp2f(M - mb);
+    Lsum *= r;
+    a.x *= r;
+    a.y *= r;
+    a.z *= r;
+    a.w *= r;
+    M = mb;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const float w = ml[i].y > 0.f ? exp2f(ml[i].x - M) : 0.f;
+      Lsum += w * ml[i].y;
+      a.x += w * x[i].x;
+      a.y += w * x[i].y;
+      a.z += w * x[i].z;
+      a.w += w * x[i].w;
+    }
   }
-  if (threadIdx.x == 0 && lse != nullptr)
-    lse[(size_t)b * H + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+  const float il = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
+  const size_t orow = (size_t)b * H + hg * kHG + h;
+  reinterpret_cast<float4*>(out + orow * D)[d4] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+  if (d4 == 0 && lse != nullptr) lse[orow] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------ host
-static int plan_splits(int batch, int H, int K) {
-  const int tiles = (K + kWindow + kTile - 1) / kTile;
-  const int per_seq_blocks = H / kHG;
-  int want = (512 + batch * per_seq_blocks - 1) / (batch * per_seq_blocks);
-  if (want < 1) want = 1;
-  int tiles_per_split = (tiles + want - 1) / want;
-  if (tiles_per_split < 1) tiles_per_split = 1;
-  return (tiles + tiles_per_split - 1) / tiles_per_split;
+struct DecodePlan {
+  int n_splits, split_tiles;
+};
+
+#ifndef CSA2_DECODE_MIN_SPLIT_TILES
+#define CSA2_DECODE_MIN_SPLIT_TILES 3
+#endif
+
+// Splits so that the grid stays within one resident wave of blocks (two per
+// CU on 256 CUs), with at least CSA2_DECODE_MIN_SPLIT_TILES tiles per split
+// so that the partials stay small next to the work, and at most kMaxSplits.
+static DecodePlan plan_decode(int batch, int H, int K) {
+  const int tiles = (K + kTile - 1) / kTile + kWinTiles;
+  const int units = batch * (H / kHG);
+  int tps = (tiles * units + 511) / 512;
+  if (tps < CSA2_DECODE_MIN_SPLIT_TILES) tps = CSA2_DECODE_MIN_SPLIT_TILES;
+  const int min_tps = (tiles + kMaxSplits - 1) / kMaxSplits;
+  if (tps < min_tps) tps = min_tps;
+  if (tps > tiles) tps = tiles;
+  return DecodePlan{(tiles + tps - 1) / tps, tps};
 }
-static int split_tokens_for(int n_splits, int K) {
-  const int tiles = (K + kWindow + kTile - 1) / kTile;
-  return ((tiles + n_splits - 1) / n_splits) * kTile;
+
+struct DecodeWs {
+  size_t part_o, part_ml, total;
+};
+static DecodeWs decode_ws(int batch, int H, int D, int K) {
+  const DecodePlan pl = plan_decode(batch, H, K);
+  const size_t units = (size_t)batch * (H / kHG);
+  const size_t rows = units * pl.n_splits * kHG;
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  DecodeWs w;
+  w.part_ml = 0;
+  w.part_o = a256(rows * 8);
+  w.total = pl.n_splits > 1 ? w.part_o + a256(rows * D * 4) : 256;
+  return w;
 }
 
 size_t sparse_decode_ws_bytes(int batch, int H, int D, int K) {
-  const int ns = plan_splits(batch, H, K);
-  if (ns == 1) return 256;
-  const size_t o = (size_t)batch * ns * H * D * 4;
-  const size_t ml = (size_t)batch * ns * H * 8;
-  return ((o + 255) & ~(size_t)255) + ml;
+  return decode_ws(batch, H, D, K).total;
 }
 
 template <int D>
 static void launch_decode(const CacheArgs& c, const int32_t* ctx_len, int H, const uint16_t* q,
                           float scale, const int32_t* idx, const int32_t* idx_count, int K,
-                          const uint16_t* swa, float* out, float* lse, float* po, float2* pml,
-                          int ns, int st_tok, hipStream_t st) {
+                          const uint16_t* swa, float* out, float* lse, uint8_t* ws,
+                          hipStream_t st) {
   const PageLayout lay = page_layout(D, c.Di);
-  const int units = c.batch * ns;
-  const int blocks = ((units + 7) / 8) * 8 * (H / kHG);
+  const DecodePlan pl = plan_decode(c.batch, H, K);
+  const DecodeWs w = decode_ws(c.batch, H, D, K);
+  const int units = c.batch * (H / kHG);
+  const int blocks = ((units + 7) / 8) * 8 * pl.n_splits;
   hipLaunchKernelGGL((sparse_decode_kernel<D>), dim3(blocks), dim3(kBlock), 0, st,
                      (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
                      lay.scales_off, lay.page_bytes, ctx_len, H, q, scale, idx, idx_count, K, swa,
-                     out, lse, po, pml, c.batch, ns, st_tok);
+                     out, lse, reinterpret_cast<float*>(ws + w.part_o),
+                     reinterpret_cast<float2*>(ws + w.part_ml), c.batch, pl.n_splits,
+                     pl.split_tiles);
+  if (pl.n_splits > 1) {
+    constexpr int HPB = kBlock / (D / 4);
+    hipLaunchKernelGGL((sparse_combine_kernel<D>), dim3(units * (kHG / HPB)), dim3(kBlock), 0, st,
+                       reinterpret_cast<const float*>(ws + w.part_o),
+                       reinterpret_cast<const float2*>(ws + w.part_ml), H, pl.n_splits, out, lse);
+  }
 }
 
 hipError_t run_sparse_decode(const CacheArgs& c, const int32_t* ctx_len, int H,
                              const uint16_t* q, float scale, const int32_t* idx,
                              const int32_t* idx_count, int K, const uint16_t* swa, float* out,
                              float* lse, void* ws, hipStream_t st) {
-  const int ns = plan_splits(c.batch, H, K);
-  const int st_tok = split_tokens_for(ns, K);
-  float* po = nullptr;
-  float2* pml = nullptr;
-  if (ns > 1) {
-    const size_t o = (size_t)c.batch * ns * H * c.D * 4;
-    po = static_cast<float*>(ws);
-    pml = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + ((o + 255) & ~(size_t)255));
-  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
   switch (c.D) {
-    case 128: launch_decode<128>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, po, pml, ns, st_tok, st); break;
-    case 256: launch_decode<256>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, po, pml, ns, st_tok, st); break;
-    case 512: launch_decode<512>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, po, pml, ns, st_tok, st); break;
+    case 128: launch_decode<128>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, w, st); break;
+    case 256: launch_decode<256>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, w, st); break;
+    case 512: launch_decode<512>(c, ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse, w, st); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL(sparse_combine_kernel, dim3(c.batch * H), dim3(128), 0, st, po, pml, H, c.D,
-                     ns, out, lse);
   return hipGetLastError();
 }
 

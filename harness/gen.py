@@ -101,7 +101,7 @@ def ctx_lens(wl: Workload) -> np.ndarray:
 
 
 def max_pages_per_seq(wl: Workload) -> int:
-    return -(-(wl.L + wl.append_steps) // PAGE)
+    return max(1, -(-(wl.L + wl.append_steps) // PAGE))
 
 
 def page_table(wl: Workload, lens: np.ndarray | None = None) -> tuple[np.ndarray, int]:
@@ -117,7 +117,7 @@ def page_table(wl: Workload, lens: np.ndarray | None = None) -> tuple[np.ndarray
         pt = np.arange(wl.B * mp, dtype=np.int32).reshape(wl.B, mp)
         return pt, wl.B * mp
     need = -(-(lens.astype(np.int64) + wl.append_steps) // PAGE)
-    total = int(need.sum())
+    total = max(1, int(need.sum()))      # a cache holds at least one page
     perm = _rng(wl, T_PERM).permutation(total).astype(np.int32)
     pt = np.full((wl.B, mp), -1, dtype=np.int32)
     off = 0
