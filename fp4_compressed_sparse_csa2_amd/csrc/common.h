@@ -49,9 +49,10 @@ __device__ __forceinline__ int sum_oct(int v) {
   return v;
 }
 
-// Exclusive prefix sum over a 256-thread block; returns the prefix, sets *total.
-// `scratch` must hold 4 ints of shared memory.  Contains barriers: every thread
-// of the block must call it.
+// Exclusive prefix sum over an NT-thread block; returns the prefix, sets *total.
+// `scratch` must hold NT/64 ints of shared memory.  Contains barriers: every
+// thread of the block must call it.
+template <int NT = kBlock>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -64,7 +65,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kBlock / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     int s = scratch[w];
     base += (w < wave) ? s : 0;
     tot += s;

@@ -19,6 +19,29 @@ struct CacheArgs {
 
 hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st);
 
+// One selection call over per-sequence int32 scores (see select.hip).  The
+// entries of sequence b are 0 <= i < n_b with n_b from ctx_len (candidates
+// of a Full layer, i = position) or from pool_count (a Reindex layer's pool,
+// output id = pool[b][i]).
+struct SelectArgs {
+  const int32_t* ctx_len;     // Full layer: n_b = clamp(ctx_len[b]) - 128
+  int max_ctx;
+  int max_pages;
+  const int32_t* pool;        // Reindex layer (non-NULL): [batch][P]
+  const int32_t* pool_count;
+  int P;
+  int batch;
+  int K;
+  const int32_t* scores;      // [batch][stride]
+  int stride;                 // multiple of 64
+  uint32_t* hist1;            // [batch][kCtrlWords], zero outside a call
+  uint2* cand;                // [batch][stride]
+  uint32_t* chunk_counts;     // [batch][kMaxSelChunks]
+  int32_t* out_idx;           // [batch][K]
+  int32_t* out_count;         // [batch]
+};
+hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st);
+
 hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, const int8_t* key,
                                const int32_t* seq, const int32_t* pos, uint16_t* swa,
                                hipStream_t st);

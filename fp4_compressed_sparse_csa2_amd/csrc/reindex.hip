@@ -8,11 +8,11 @@
 // recomputes index / candidates (zulogic "DeepSeek V4 1-Flash 架构拆解",
 // section 3 table).  The indexer keys are the owner's, shared by all layers.
 //
-// One kernel: blocks of 256 pool entries gather the keys (each entry's 64 or
-// 128 key bytes read by 4 or 8 lanes), score them with v_dot4 and histogram
-// the top digit; the last block of each sequence fixes the exact threshold
-// and emits the winners in ascending pool order (= ascending position, the
-// pool being ascending).
+// The score kernel gathers the keys of blocks of 256 pool entries (each
+// entry's 64 or 128 key bytes read by 4 or 8 lanes), scores them with v_dot4
+// and histograms the top digit; the selection kernels of select.hip then
+// take Top-K' over the pool entries, which are in ascending position order,
+// and map the winners back to positions.
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -20,41 +20,31 @@
 namespace csa2 {
 
 constexpr int kREntries = 256;          // pool entries per block
-constexpr int kRCtrlWords = kBins + 64; // hist1 [2048], done at kBins
 
 template <int DI>
-__global__ __launch_bounds__(kBlock) void reindex_kernel(
+__global__ __launch_bounds__(kBlock) void reindex_score_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
     int max_pages, int keys_off, int page_bytes, const int8_t* __restrict__ q_idx,
     const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_count, int P, int K,
-    int32_t* __restrict__ scores, uint32_t* __restrict__ ctrl, int32_t* __restrict__ out_idx,
-    int32_t* __restrict__ out_count) {
+    int32_t* __restrict__ scores, int stride, int32_t* __restrict__ out_scores,
+    uint32_t* __restrict__ ctrl) {
   constexpr int LPP = DI / 16;
   constexpr int PPL = 64 / LPP;
   __shared__ uint32_t hist[kBins];
-  __shared__ int scan_scratch[4];
-  __shared__ int sh_t1, sh_above1, sh_t2, sh_above2, sh_last;
 
   const int b = blockIdx.y;
   int c = pool_count[b];
   c = c < 0 ? 0 : (c > P ? P : c);
   const int e0 = blockIdx.x * kREntries;
+  const bool do_hist = K > 0 && c > K;          // a selection will run
+  if (e0 >= c || (!do_hist && out_scores == nullptr)) return;
   const int32_t* prow = pool + (size_t)b * P;
-  int32_t* out = out_idx + (size_t)b * K;
+  int32_t* sc_row = scores + (size_t)b * stride;
 
-  if (K == 0 || c <= K) {               // every pool entry survives
-    for (int i = e0 + threadIdx.x; i < e0 + kREntries && i < K; i += kBlock)
-      out[i] = i < c ? prow[i] : -1;
-    if (blockIdx.x == 0 && threadIdx.x == 0) out_count[b] = c < K ? c : K;
-    return;
+  if (do_hist) {
+    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+    __syncthreads();
   }
-  if (e0 >= c) return;
-  const int n_blocks = (c + kREntries - 1) / kREntries;
-  uint32_t* cb = ctrl + (size_t)b * kRCtrlWords;
-  int32_t* sc_row = scores + (size_t)b * P;
-
-  for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
-  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
@@ -94,69 +84,78 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(
     // an unusable entry (contract violation) ranks below every real score
     const int s = keep_ok ? keep : -kKeyBias;
     sc_row[e] = s;
-    atomicAdd(&hist[score_key(s) >> 11], 1u);
+    if (out_scores != nullptr) out_scores[(size_t)b * P + e] = s;
+    if (do_hist) atomicAdd(&hist[score_key(s) >> 11], 1u);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += kBlock) {
-    const uint32_t h = hist[i];
-    if (h) atomicAdd(&cb[i], h);
+  if (do_hist) {
+    __syncthreads();
+    uint32_t* g = ctrl + (size_t)b * kCtrlWords;
+    for (int i = threadIdx.x; i < kBins; i += kBlock) {
+      const uint32_t h = hist[i];
+      if (h) atomicAdd(&g[i], h);
+    }
   }
-
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) sh_last = (atomicAdd(&cb[kBins], 1u) == (uint32_t)(n_blocks - 1));
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-
-  // last block of this sequence: exact threshold over the whole pool
-  find_digit(cb, K, scan_scratch, &sh_t1, &sh_above1);
-  const uint32_t t1 = (uint32_t)sh_t1;
-  for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < c; i += kBlock) {
-    const uint32_t key = score_key(sc_row[i]);
-    if ((key >> 11) == t1) atomicAdd(&hist[key & (kBins - 1)], 1u);
-  }
-  __syncthreads();
-  const int need1 = K - sh_above1;
-  find_digit(hist, need1, scan_scratch, &sh_t2, &sh_above2);
-  const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
-  const int need_ties = need1 - sh_above2;
-  // the pool is ascending, so pool order is position order
-  const int written = emit_in_order(
-      [&](int i) { return make_uint2(score_key(sc_row[i]), (uint32_t)prow[i]); }, c, tau,
-      need_ties, out, K, scan_scratch);
-  for (int j = written + threadIdx.x; j < K; j += kBlock) out[j] = -1;
-  if (threadIdx.x == 0) out_count[b] = written;
-  for (int i = threadIdx.x; i < kRCtrlWords; i += kBlock) cb[i] = 0u;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t reindex_ws_bytes(int batch, int P, int /*K*/) {
-  return align256((size_t)batch * kRCtrlWords * 4) + align256((size_t)batch * P * 4);
+struct ReindexWs {
+  size_t ctrl, counts, scores, cand, total;
+};
+static ReindexWs reindex_ws(int batch, int P) {
+  const size_t stride = (size_t)row_stride(P);
+  ReindexWs w;
+  w.ctrl = 0;
+  w.counts = align256((size_t)batch * kCtrlWords * 4);
+  w.scores = w.counts + align256((size_t)batch * kMaxSelChunks * 4);
+  w.cand = w.scores + align256((size_t)batch * stride * 4);
+  w.total = w.cand + align256((size_t)batch * stride * 8);
+  return w;
 }
+
+size_t reindex_ws_bytes(int batch, int P, int /*K*/) { return reindex_ws(batch, P).total; }
 
 hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* pool,
                        const int32_t* pool_count, int P, int K, int32_t* out_idx,
                        int32_t* out_count, int32_t* out_scores, void* ws, hipStream_t st) {
-  uint32_t* ctrl = static_cast<uint32_t*>(ws);
-  int32_t* scores = out_scores ? out_scores
-                               : reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
-                                                            align256((size_t)c.batch * kRCtrlWords * 4));
+  const ReindexWs w = reindex_ws(c.batch, P);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + w.ctrl);
+  int32_t* scores = reinterpret_cast<int32_t*>(base + w.scores);
+  const int stride = row_stride(P);
   const PageLayout lay = page_layout(c.D, c.Di);
-  const int span = P > K ? P : K;
-  const dim3 grid(span > 0 ? (span + kREntries - 1) / kREntries : 1, c.batch);
-  if (c.Di == 128)
-    hipLaunchKernelGGL(reindex_kernel<128>, grid, dim3(kBlock), 0, st, (const uint8_t*)c.pages,
-                       c.page_table, c.num_pages, c.max_pages, lay.keys_off, lay.page_bytes,
-                       q_idx, pool, pool_count, P, K, scores, ctrl, out_idx, out_count);
-  else
-    hipLaunchKernelGGL(reindex_kernel<64>, grid, dim3(kBlock), 0, st, (const uint8_t*)c.pages,
-                       c.page_table, c.num_pages, c.max_pages, lay.keys_off, lay.page_bytes,
-                       q_idx, pool, pool_count, P, K, scores, ctrl, out_idx, out_count);
-  return hipGetLastError();
+  if (P > 0) {
+    const dim3 grid((P + kREntries - 1) / kREntries, c.batch);
+    if (c.Di == 128)
+      hipLaunchKernelGGL(reindex_score_kernel<128>, grid, dim3(kBlock), 0, st,
+                         (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
+                         lay.keys_off, lay.page_bytes, q_idx, pool, pool_count, P, K, scores,
+                         stride, out_scores, ctrl);
+    else
+      hipLaunchKernelGGL(reindex_score_kernel<64>, grid, dim3(kBlock), 0, st,
+                         (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
+                         lay.keys_off, lay.page_bytes, q_idx, pool, pool_count, P, K, scores,
+                         stride, out_scores, ctrl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  SelectArgs a;
+  a.ctx_len = nullptr;
+  a.max_ctx = 0;
+  a.max_pages = c.max_pages;
+  a.pool = pool;
+  a.pool_count = pool_count;
+  a.P = P;
+  a.batch = c.batch;
+  a.K = K;
+  a.scores = scores;
+  a.stride = stride;
+  a.hist1 = ctrl;
+  a.cand = reinterpret_cast<uint2*>(base + w.cand);
+  a.chunk_counts = reinterpret_cast<uint32_t*>(base + w.counts);
+  a.out_idx = out_idx;
+  a.out_count = out_count;
+  return run_select(a, P, st);
 }
 
 }  // namespace csa2

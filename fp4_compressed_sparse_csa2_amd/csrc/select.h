@@ -13,27 +13,31 @@
 
 namespace csa2 {
 
-// The 8 histogram bins thread i scans, top first: h[k] = hist[2047 - 8i - k].
+// Per-sequence control words of a selection (uint32): the top-digit histogram
+// the scoring kernel fills, then spare words.  The size does not depend on the
+// call's sizes, so a zeroed workspace stays zeroed between calls of any shape.
+constexpr int kCtrlWords = kBins + 64;
+constexpr int kMaxSelChunks = 4096;      // 4096-entry filter chunks of a 2^24-entry sequence
+constexpr int kSingleMax = 1 << 17;      // longest sequence for the one-block selection
+
+// Row stride (in entries) of score and candidate arrays: a multiple of 64 so
+// that every row starts 256-byte aligned.
+__host__ __device__ inline int row_stride(int n) { return (n + 63) & ~63; }
+
+// The bins thread i of an NT-thread block scans, top first:
+// h[k] = hist[2047 - BPT*i - k], BPT = 2048 / NT.
+template <int NT>
 struct DigitBins {
-  int h[8];
+  static constexpr int BPT = kBins / NT;
+  int h[BPT];
 };
 
-template <typename HistT>
-__device__ __forceinline__ DigitBins load_digit_bins(const HistT* hist) {
-  DigitBins d;
-  const int top = kBins - 8 * (int)threadIdx.x;
+template <int NT = kBlock, typename HistT>
+__device__ __forceinline__ DigitBins<NT> load_digit_bins(const HistT* hist) {
+  DigitBins<NT> d;
+  const int top = kBins - DigitBins<NT>::BPT * (int)threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) d.h[k] = (int)hist[top - 1 - k];
-  return d;
-}
-
-// Same from a 16-byte aligned global histogram with two 16-byte loads.
-__device__ __forceinline__ DigitBins load_digit_bins_vec(const uint32_t* hist) {
-  const uint4* p = reinterpret_cast<const uint4*>(hist + kBins - 8 * (int)threadIdx.x - 8);
-  const uint4 lo = p[0], hi = p[1];
-  DigitBins d;
-  d.h[0] = (int)hi.w; d.h[1] = (int)hi.z; d.h[2] = (int)hi.y; d.h[3] = (int)hi.x;
-  d.h[4] = (int)lo.w; d.h[5] = (int)lo.z; d.h[6] = (int)lo.y; d.h[7] = (int)lo.x;
+  for (int k = 0; k < DigitBins<NT>::BPT; ++k) d.h[k] = (int)hist[top - 1 - k];
   return d;
 }
 
@@ -41,20 +45,22 @@ __device__ __forceinline__ DigitBins load_digit_bins_vec(const uint32_t* hist) {
 // count strictly above it, from the bins each thread holds.  All threads must
 // call; results land in *t_out / *above_out (shared) and are visible to every
 // thread on return.  If the histogram holds fewer than `need` entries,
-// *t_out = -1.
-__device__ inline void find_digit_in(const DigitBins& d, int need, int* scan_scratch, int* t_out,
-                                     int* above_out) {
-  const int top = kBins - 8 * (int)threadIdx.x;
+// *t_out = -1.  `scan_scratch`: NT/64 shared ints.
+template <int NT = kBlock>
+__device__ inline void find_digit_in(const DigitBins<NT>& d, int need, int* scan_scratch,
+                                     int* t_out, int* above_out) {
+  constexpr int BPT = DigitBins<NT>::BPT;
+  const int top = kBins - BPT * (int)threadIdx.x;
   int s = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s += d.h[k];
+  for (int k = 0; k < BPT; ++k) s += d.h[k];
   if (threadIdx.x == 0) *t_out = -1;
   int total;
-  const int excl = block_exclusive_scan(s, scan_scratch, &total);
+  const int excl = block_exclusive_scan<NT>(s, scan_scratch, &total);
   if (excl < need && need <= excl + s) {
     int run = excl;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < BPT; ++k) {
       if (run + d.h[k] >= need) {
         *t_out = top - 1 - k;
         *above_out = run;
@@ -66,10 +72,10 @@ __device__ inline void find_digit_in(const DigitBins& d, int need, int* scan_scr
   __syncthreads();
 }
 
-template <typename HistT>
+template <int NT = kBlock, typename HistT>
 __device__ void find_digit(const HistT* hist, int need, int* scan_scratch, int* t_out,
                            int* above_out) {
-  find_digit_in(load_digit_bins(hist), need, scan_scratch, t_out, above_out);
+  find_digit_in<NT>(load_digit_bins<NT>(hist), need, scan_scratch, t_out, above_out);
 }
 
 constexpr int kEmitPerThread = 8;   // entries per thread per round of the emission
@@ -78,15 +84,15 @@ constexpr int kEmitPerThread = 8;   // entries per thread per round of the emiss
 //   get(f) -> uint2{key, id} for f < total, ids strictly ascending in f.
 //   key > tau: selected; key == tau: the first `need_ties` of them (lowest
 //   ids) are selected; key < tau: dropped.
-// Writes out[j] = id of the j-th selected entry (ascending ids) for j < K and
-// returns the number selected (uniform).  `scan_scratch`: 4 shared ints.
+// Calls put(j, id) for the j-th selected entry (ascending ids), j < K, and
+// returns the number selected (uniform).  `scan_scratch`: NT/64 shared ints.
 // All threads must call.
-template <typename Get>
-__device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, int32_t* out,
-                             int K, int* scan_scratch) {
+template <int NT = kBlock, typename Get, typename Put>
+__device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, int K,
+                             int* scan_scratch, Put put) {
   constexpr int E = kEmitPerThread;
   int carry_gt = 0, carry_tie = 0;
-  for (int base = 0; base < total; base += kBlock * E) {
+  for (int base = 0; base < total; base += NT * E) {
     const int f0 = base + (int)threadIdx.x * E;
     uint2 c[E];
     int n_gt = 0, n_tie = 0;
@@ -97,19 +103,19 @@ __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, in
       n_gt += (live && c[e].x > tau) ? 1 : 0;
       n_tie += (live && c[e].x == tau) ? 1 : 0;
     }
-    // one scan carries both counts: per round each is <= 256 * E < 2^16
+    // one scan carries both counts: per round each is <= NT * E < 2^16
     int round_total;
-    const int pre = block_exclusive_scan(n_gt | (n_tie << 16), scan_scratch, &round_total);
+    const int pre = block_exclusive_scan<NT>(n_gt | (n_tie << 16), scan_scratch, &round_total);
     int g = carry_gt + (pre & 0xFFFF), t = carry_tie + (pre >> 16);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (f0 + e >= total) break;
       if (c[e].x > tau) {
         const int slot = g + (t < need_ties ? t : need_ties);
-        if (slot < K) out[slot] = (int32_t)c[e].y;
+        if (slot < K) put(slot, c[e].y);
         ++g;
       } else if (c[e].x == tau) {
-        if (t < need_ties && g + t < K) out[g + t] = (int32_t)c[e].y;
+        if (t < need_ties && g + t < K) put(g + t, c[e].y);
         ++t;
       }
     }

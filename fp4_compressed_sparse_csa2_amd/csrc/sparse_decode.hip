@@ -8,15 +8,16 @@
 // Reuse layer attends with its own queries over reused indices (same page,
 // section 3).  One latent row per token is both key and value.
 //
-// Work: a sequence's tokens form 64-token tiles -- ceil(K/64) tiles of
-// selected FP4 rows, then two tiles of window rows.  A block owns one
+// Work: a sequence's tokens form 64-token tiles -- two tiles of window rows,
+// then ceil(K/64) tiles of selected FP4 rows.  A block owns one
 // (sequence, group of 16 heads) and a run of consecutive tiles (a split);
 // 4 waves.  All splits of one (sequence, head group) land on one XCD.
 //
-// The block starts by loading, all at once, its queries, the indices of its
-// first run of up to 8 tiles and (when it fits in LDS) the sequence's page
-// table; per run it then resolves every row address and keeps the FP4 rows of
-// the next tile in flight (registers) while it computes the current one:
+// The block starts by loading, all at once, its queries, its first window
+// rows, the positions of its first four FP4 tiles and (when it fits in LDS)
+// the sequence's page table.  The FP4 tiles then run as a pipeline: while
+// tile f computes, the rows of f+1, the page of f+3 and the position of f+4
+// are in flight.  Per tile:
 //   1. dequantise the tile into LDS as f16 [64][D+8] (FP4 -> exact E2M1 with
 //      the hardware converter at scale 1.0, then an exact f16 multiply by the
 //      E4M3 scale; window rows bf16 -> f16, exact);
@@ -50,7 +51,6 @@ __device__ __forceinline__ half4 lds_read_tr(const _Float16* p) {
 constexpr int kTile = 64;                  // tokens per tile
 constexpr int kHG = 16;                    // heads per block
 constexpr int kPStride = kTile + 8;        // P tile row stride (halfs)
-constexpr int kRun = 8;                    // tiles whose metadata is loaded together
 constexpr int kWinTiles = kWindow / kTile; // window tiles per sequence
 constexpr int kMaxSplits = 64;
 constexpr int kPtCache = 2048;             // page-table entries cached in LDS (131072 positions)
@@ -95,13 +95,16 @@ struct RowPart {
   uint2 s;
 };
 
+// Loads one thread's quarter of the row rowkey = (page << 6) | row; a negative
+// rowkey loads row 0 of page 0 instead (always present), so that the loads of
+// a pipeline stage are issued without branches.
 template <int D>
 __device__ __forceinline__ void load_row_part(RowPart<D>& r, const uint8_t* pages,
                                               long long rowkey, int page_bytes, int scales_off,
                                               int g_q) {
-  if (rowkey < 0) return;
-  const uint8_t* page = pages + (size_t)(rowkey >> 6) * page_bytes;
-  const int row = (int)(rowkey & 63);
+  const long long rk = rowkey < 0 ? 0 : rowkey;
+  const uint8_t* page = pages + (size_t)(rk >> 6) * page_bytes;
+  const int row = (int)(rk & 63);
   const uint4* cp = reinterpret_cast<const uint4*>(page + row * (D / 2) + g_q * (D / 8));
 #pragma unroll
   for (int i = 0; i < D / 128; ++i) r.c[i] = cp[i];
@@ -115,7 +118,8 @@ __device__ __forceinline__ void load_row_part(RowPart<D>& r, const uint8_t* page
   }
 }
 
-template <int D>
+// PTC: the sequence's page table (max_pages <= kPtCache) is staged in LDS.
+template <int D, bool PTC>
 __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
     int max_pages, int scales_off, int page_bytes, const int32_t* __restrict__ ctx_len, int H,
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   __shared__ float red_max[4][kHG];
   __shared__ float red_sum[4][kHG];
   __shared__ uint8_t valid[kTile];
-  __shared__ int pt_lds[kPtCache];
+  __shared__ int pt_lds[PTC ? kPtCache : 1];
 
   // ---- block -> (unit = (sequence, head group), split); a unit's splits share an XCD
   const int n_hg = H / kHG;
@@ -149,11 +153,15 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   int cnt = idx_count[b];
   cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
   const int n_win = L < kWindow ? L : kWindow;
-  const int tf_plan = (K + kTile - 1) / kTile;           // FP4 tiles of the plan
-  const int tf = (cnt + kTile - 1) / kTile;              // FP4 tiles holding tokens
-  const int tw = (n_win + kTile - 1) / kTile;            // window tiles holding tokens
+  // the sequence's tiles: [window 0, window 1, FP4 0, FP4 1, ...]
+  const int tf_plan = (K + kTile - 1) / kTile;
   const int t_begin = split * split_tiles;
-  const int t_end = min(t_begin + split_tiles, tf_plan + kWinTiles);
+  const int t_end = min(t_begin + split_tiles, kWinTiles + tf_plan);
+  const int tw = (n_win + kTile - 1) / kTile;            // window tiles holding tokens
+  const int tf = (cnt + kTile - 1) / kTile;              // FP4 tiles holding tokens
+  const int wa = t_begin, wb = min(t_end, tw);           // this block's window tiles
+  const int fa = max(t_begin - kWinTiles, 0);            // this block's FP4 tiles [fa, fb)
+  const int fb = min(t_end - kWinTiles, tf);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
@@ -163,27 +171,42 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const int32_t* idx_row = idx + (size_t)b * K;
   const uint16_t* swa_b = swa + (size_t)b * kWindow * D;
-  const int f_begin = t_begin, f_end = min(t_end, tf);
 
-  // indices of the first run of FP4 tiles
-  int pos[kRun];
-  auto load_pos = [&](int r0) {
-    const int nr = min(kRun, f_end - r0);
+  // ---- prologue: every load that depends on nothing is issued here
+  // window rows of the first window tile (token k of the window is position L - n_win + k)
+  uint4 wreg[DQ / 8];
+  auto load_win = [&](int t) {
+    const int k = t * kTile + g_tok;
+    const int p = L - n_win + (k < n_win ? k : 0);
+    const uint4* src = reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + g_q * DQ);
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      const int j = (r0 + i) * kTile + g_tok;
-      pos[i] = (i < nr && j < cnt) ? idx_row[j] : -1;
-    }
+    for (int i = 0; i < DQ / 8; ++i) wreg[i] = src[i];
   };
-  if (f_begin < f_end) load_pos(f_begin);
-  // the sequence's page table, into LDS when it fits
-  const bool pt_cached = max_pages <= kPtCache && f_begin < f_end;
-  int ptv[kPtCache / kBlock];
-  if (pt_cached) {
+  if (wa < wb) load_win(wa);
+  // positions of the first FP4 tiles.  A position is carried as the raw
+  // loaded index (an unconditional load of a clamped address) plus a flag
+  // computed without it, so that no load result is consumed in the stage
+  // that issues it.
+  auto pos_load = [&](int f) -> int {
+    const int j = f * kTile + g_tok;
+    return idx_row[j < cnt ? j : cnt - 1];
+  };
+  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + g_tok < cnt; };
+  int p0 = -1, p1 = -1, p2 = -1, p3 = -1;
+  bool ok3 = false;
+  if (fa < fb) {
+    p0 = pos_load(fa);
+    p1 = pos_load(fa + 1);
+    p2 = pos_load(fa + 2);
+    p3 = pos_load(fa + 3);
+    ok3 = pos_ok(fa + 3);
+  }
+  int ptv[PTC ? kPtCache / kBlock : 1];
+  if (PTC && fa < fb) {
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i) {
       const int e = i * kBlock + tid;
-      ptv[i] = e < max_pages ? pt[e] : -1;
+      ptv[i] = pt[e < max_pages ? e : 0];
     }
   }
 
@@ -219,11 +242,35 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   }
   // logits in log2 units: scale2 * (q~ . x)
   const float scale2 = ldexpf(scale, -qexp) * kLog2e;
-  if (pt_cached) {
+  if (PTC && fa < fb) {
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i) pt_lds[i * kBlock + tid] = ptv[i];
   }
   __syncthreads();
+
+  // page of a selected position (-1 if it is not a selectable position)
+  auto page_of = [&](int p) -> int {
+    const bool in = p >= 0 && p < n_glob;
+    const int pi = in ? p / kPage : 0;
+    const int v = PTC ? pt_lds[pi] : pt[pi];
+    return in ? v : -1;
+  };
+  auto rowkey_of = [&](int p, int pg) -> long long {
+    return (p >= 0 && pg >= 0 && pg < num_pages) ? ((long long)pg << 6) | (p & (kPage - 1)) : -1;
+  };
+  int pg2 = -1;
+  long long rk0 = -1, rk1 = -1;
+  RowPart<D> cur, nxt;
+  if (fa < fb) {
+    p0 = pos_ok(fa) ? p0 : -1;
+    p1 = pos_ok(fa + 1) ? p1 : -1;
+    p2 = pos_ok(fa + 2) ? p2 : -1;
+    const int pg0 = page_of(p0), pg1 = page_of(p1);
+    pg2 = page_of(p2);
+    rk0 = rowkey_of(p0, pg0);
+    rk1 = rowkey_of(p1, pg1);
+    load_row_part<D>(cur, pages, rk0, page_bytes, scales_off, g_q);
+  }
 
   // running softmax state: per lane for head lc (QK layout) and for heads
   // 4lg+i (PV layout); identical inputs give identical values in both.
@@ -233,7 +280,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- compute one tile that sits in X (valid[] marks real tokens)
+  // ---- one tile that sits in X (valid[] marks real tokens)
   auto compute_tile = [&]() {
     // S^T for tokens 16*wave .. +16 of the tile, all 16 heads
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
@@ -310,67 +357,50 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 
   _Float16* xrow = X + g_tok * XS + g_q * DQ;
 
-  // ---- FP4 tiles of this split, in runs of kRun
-  for (int r0 = f_begin; r0 < f_end; r0 += kRun) {
-    const int nr = min(kRun, f_end - r0);
-    if (r0 != f_begin) load_pos(r0);
-    long long rowkey[kRun];
+  // ---- window tiles (their rows were requested in the prologue)
+#pragma unroll 1
+  for (int t = wa; t < wb; ++t) {
+    const bool ok = t * kTile + g_tok < n_win;
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      const int p = pos[i];
-      const bool in = p >= 0 && p < n_glob;
-      const int pg = !in ? -1 : (pt_cached ? pt_lds[p / kPage] : pt[p / kPage]);
-      rowkey[i] = (pg >= 0 && pg < num_pages) ? ((long long)pg << 6) | (p % kPage) : -1;
-    }
-    RowPart<D> cur, nxt;
-    load_row_part<D>(cur, pages, rowkey[0], page_bytes, scales_off, g_q);
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      if (i >= nr) break;
-      if (i + 1 < nr) load_row_part<D>(nxt, pages, rowkey[i + 1], page_bytes, scales_off, g_q);
-      const bool ok = rowkey[i] >= 0;
-      if (ok) {
-#pragma unroll
-        for (int g = 0; g < DQ / 16; ++g) {
-          const uint4 c4 = cur.c[g / 2];
-          const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
-          const uint32_t sc = ((g < 4 ? cur.s.x : cur.s.y) >> (8 * (g & 3))) & 0xFFu;
-          half8 lo, hi;
-          dequant16(w0, w1, sc, lo, hi);
-          *reinterpret_cast<half8*>(xrow + 16 * g) = lo;
-          *reinterpret_cast<half8*>(xrow + 16 * g + 8) = hi;
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < DQ / 8; ++k) *reinterpret_cast<half8*>(xrow + 8 * k) = half8{};
-      }
-      if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
-      __syncthreads();
-      compute_tile();
-      cur = nxt;
-    }
+    for (int i = 0; i < DQ / 8; ++i)
+      *reinterpret_cast<half8*>(xrow + 8 * i) = ok ? bf16x8_to_f16(wreg[i]) : half8{};
+    if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
+    if (t + 1 < wb) load_win(t + 1);    // in flight while this tile computes
+    __syncthreads();
+    compute_tile();
   }
 
-  // ---- window tiles of this split
-  for (int t = max(t_begin, tf_plan); t < t_end; ++t) {
-    const int w = t - tf_plan;
-    if (w >= tw) break;
-    const int k = w * kTile + g_tok;
-    const bool ok = k < n_win;
-    if (ok) {
-      const int p = L - n_win + k;
-      const uint4* src =
-          reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + g_q * DQ);
+  // ---- FP4 tiles: a pipeline position -> page -> row address -> rows, so
+  // that tile f computes while the rows of f+1, the page of f+3 and the
+  // position of f+4 are on their way
+#pragma unroll 1
+  for (int f = fa; f < fb; ++f) {
+    load_row_part<D>(nxt, pages, rk1, page_bytes, scales_off, g_q);
+    const long long rk2 = rowkey_of(p2, pg2);
+    const int pg3 = page_of(ok3 ? p3 : -1);
+    const int p4 = pos_load(f + 4);          // consumed next iteration
+    const bool ok4 = pos_ok(f + 4);
+    const bool ok = rk0 >= 0;
 #pragma unroll
-      for (int i = 0; i < DQ / 8; ++i)
-        *reinterpret_cast<half8*>(xrow + 8 * i) = bf16x8_to_f16(src[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < DQ / 8; ++i) *reinterpret_cast<half8*>(xrow + 8 * i) = half8{};
+    for (int g = 0; g < DQ / 16; ++g) {
+      const uint4 c4 = cur.c[g / 2];
+      const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
+      const uint32_t sc = ((g < 4 ? cur.s.x : cur.s.y) >> (8 * (g & 3))) & 0xFFu;
+      half8 lo, hi;
+      dequant16(w0, w1, sc, lo, hi);
+      *reinterpret_cast<half8*>(xrow + 16 * g) = ok ? lo : half8{};
+      *reinterpret_cast<half8*>(xrow + 16 * g + 8) = ok ? hi : half8{};
     }
     if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
     __syncthreads();
     compute_tile();
+    rk0 = rk1;
+    rk1 = rk2;
+    p2 = ok3 ? p3 : -1;
+    pg2 = pg3;
+    p3 = p4;
+    ok3 = ok4;
+    cur = nxt;
   }
 
   // ---- finish: total l per head across waves (every wave saw the same m)
@@ -411,7 +441,6 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
     part_ml[(ubase + split) * kHG + lc] = make_float2(m_q, lt);
   }
-
 }
 
 // LSE merge of the split partials.  Block = (unit, HPB heads); thread = one
@@ -528,10 +557,12 @@ static void launch_decode(const CacheArgs& c, const int32_t* ctx_len, int H, con
   const DecodeWs w = decode_ws(c.batch, H, D, K);
   const int units = c.batch * (H / kHG);
   const int blocks = ((units + 7) / 8) * 8 * pl.n_splits;
-  hipLaunchKernelGGL((sparse_decode_kernel<D>), dim3(blocks), dim3(kBlock), 0, st,
-                     (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                     lay.scales_off, lay.page_bytes, ctx_len, H, q, scale, idx, idx_count, K, swa,
-                     out, lse, reinterpret_cast<float*>(ws + w.part_o),
+  auto kern = c.max_pages <= kPtCache ? sparse_decode_kernel<D, true>
+                                      : sparse_decode_kernel<D, false>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBlock), 0, st, (const uint8_t*)c.pages,
+                     c.page_table, c.num_pages, c.max_pages, lay.scales_off, lay.page_bytes,
+                     ctx_len, H, q, scale, idx, idx_count, K, swa, out, lse,
+                     reinterpret_cast<float*>(ws + w.part_o),
                      reinterpret_cast<float2*>(ws + w.part_ml), c.batch, pl.n_splits,
                      pl.split_tiles);
   if (pl.n_splits > 1) {
