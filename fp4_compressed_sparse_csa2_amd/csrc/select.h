@@ -18,7 +18,7 @@ namespace csa2 {
 // call's sizes, so a zeroed workspace stays zeroed between calls of any shape.
 constexpr int kCtrlWords = kBins + 64;
 constexpr int kMaxSelChunks = 4096;      // 4096-entry filter chunks of a 2^24-entry sequence
-constexpr int kSingleMax = 1 << 17;      // longest sequence for the one-block selection
+constexpr int kSingleMax = 1 << 14;      // longest sequence for the one-block selection
 
 // Row stride (in entries) of score and candidate arrays: a multiple of 64 so
 // that every row starts 256-byte aligned.

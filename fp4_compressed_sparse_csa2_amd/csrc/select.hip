@@ -13,10 +13,11 @@
 // cross-block synchronisation inside a kernel (visibility comes from kernel
 // boundaries):
 //   single  - up to kSingleMax entries: one block per sequence finds the
-//             K-th largest top digit t1, streams the scores once keeping the
-//             entries with digit >= t1 in entry order (one block scan per
-//             round of 16K entries) and histogramming the low digit of those
-//             equal to t1, fixes the exact threshold and emits in order.
+//             K-th largest top digit t1, reads the scores once (every load of
+//             a 32K-entry round in flight together) keeping the entries with
+//             digit >= t1 in entry order (one block scan per round) and
+//             histogramming the low digit of those equal to t1, fixes the
+//             exact threshold and emits in order.
 //   filter  - longer sequences: 4096-entry blocks keep their digit >= t1
 //   + final   entries, in order, in their own slots; then one block per
 //             sequence concatenates the slot lists (already in order),
@@ -28,10 +29,11 @@
 
 namespace csa2 {
 
-constexpr int kSelNT = 1024;                     // threads of the one-block-per-sequence kernels
-constexpr int kSelPT = 16;                       // entries per thread per round
-constexpr int kSelRound = kSelNT * kSelPT;       // 16384 entries per round
-constexpr int kListCap = 6144;                   // candidates kept in LDS
+constexpr int kSelNT = 512;                      // threads of the one-block-per-sequence kernels
+constexpr int kSelPT = 64;                       // entries per thread per round
+constexpr int kSelRound = kSelNT * kSelPT;       // 32768 entries (128 KB) per round
+constexpr int kListCap = 6144;                   // candidates the final kernel keeps in LDS
+constexpr int kSingleListCap = 2944;             // candidates the single kernel keeps in LDS
 constexpr int kFiltPer = 16;                     // entries per thread in the filter kernel
 constexpr int kFiltChunk = kBlock * kFiltPer;    // 4096 entries per filter block
 
@@ -61,9 +63,14 @@ __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, in
 }
 
 // ------------------------------------------------------------------ single
+// Thread t takes the 64 entries at r * 32768 + 64t of round r; every load of
+// a round (and, for the first, the histogram) is issued before any result is
+// used, so each 32768-entry round costs one memory round trip.
+// The streaming passes touch LDS only to write the (rare) kept entries; the
+// low-digit histogram is built afterwards from the kept list.
 __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
-  __shared__ uint2 list[kListCap];
+  __shared__ uint2 list[kSingleListCap];
   __shared__ int scan_scratch[kSelNT / 64];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2;
 
@@ -78,58 +85,64 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   const int32_t* row = a.scores + (size_t)b * a.stride;
   uint2* ovf = a.cand + (size_t)b * a.stride;
+  const int rounds = (n + kSelRound - 1) / kSelRound;
 
-  // round r covers entries [r*16384, +16384); thread t the 16 at r*16384 + 16t.
   // Entry indices and the row stride are multiples of 16, so a 16-entry run
-  // that starts below n lies inside the row.
-  auto load_round = [&](int r, uint4* v) {
-    const int p0 = r * kSelRound + tid * kSelPT;
-    if (p0 < n) {
-      const uint4* src = reinterpret_cast<const uint4*>(row + p0);
+  // that starts below n lies inside the row; runs past n load entry 0.
+  uint4 v[kSelPT / 4];
+  auto load_round = [&](int r) {
 #pragma unroll
-      for (int i = 0; i < kSelPT / 4; ++i) v[i] = src[i];
+    for (int c = 0; c < kSelPT / 16; ++c) {
+      const int q0 = r * kSelRound + tid * kSelPT + 16 * c;
+      const uint4* src = reinterpret_cast<const uint4*>(row + (q0 < n ? q0 : 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * c + i] = src[i];
     }
   };
-  uint4 cur[kSelPT / 4], nxt[kSelPT / 4];
-  load_round(0, cur);
+  load_round(0);
   const DigitBins<kSelNT> bins = load_digit_bins<kSelNT>(h1);
   for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
+  // digit >= t1  <=>  score >= lo (score_key folds only the top score, which
+  // is above every threshold a digit can set)
+  const int lo = sh_t1 < 0 ? INT_MAX : (int)(t1 << 11) - kKeyBias;
 
   int total = 0;
-  const int rounds = (n + kSelRound - 1) / kSelRound;
   for (int r = 0; r < rounds; ++r) {
-    if (r + 1 < rounds) load_round(r + 1, nxt);
+    if (r > 0) load_round(r);
     const int p0 = r * kSelRound + tid * kSelPT;
-    uint32_t key[kSelPT];
     int nk = 0;
 #pragma unroll
     for (int i = 0; i < kSelPT / 4; ++i) {
-      const int w[4] = {(int)cur[i].x, (int)cur[i].y, (int)cur[i].z, (int)cur[i].w};
+      const int w[4] = {(int)v[i].x, (int)v[i].y, (int)v[i].z, (int)v[i].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bool in = p0 + 4 * i + k < n;
-        const uint32_t kk = score_key(w[k]);
-        const bool keep = in && (kk >> 11) >= t1;
-        if (in && (kk >> 11) == t1) atomicAdd(&hist2[kk & (kBins - 1)], 1u);
-        key[4 * i + k] = keep ? kk : 0u;       // every real key is >= 2^14: 0 marks "dropped"
-        nk += keep ? 1 : 0;
-      }
+      for (int k = 0; k < 4; ++k) nk += (w[k] >= lo && p0 + 4 * i + k < n) ? 1 : 0;
     }
     int round_total;
     int slot = total + block_exclusive_scan<kSelNT>(nk, scan_scratch, &round_total);
+    if (nk > 0) {
 #pragma unroll
-    for (int e = 0; e < kSelPT; ++e) {
-      if (key[e] != 0u) {
-        const uint2 c = make_uint2(key[e], (uint32_t)(p0 + e));
-        if (slot < kListCap) list[slot] = c; else ovf[slot] = c;
-        ++slot;
+      for (int i = 0; i < kSelPT / 4; ++i) {
+        const int w[4] = {(int)v[i].x, (int)v[i].y, (int)v[i].z, (int)v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int p = p0 + 4 * i + k;
+          if (w[k] >= lo && p < n) {
+            const uint2 c = make_uint2(score_key(w[k]), (uint32_t)p);
+            if (slot < kSingleListCap) list[slot] = c; else ovf[slot] = c;
+            ++slot;
+          }
+        }
       }
     }
     total += round_total;
-#pragma unroll
-    for (int i = 0; i < kSelPT / 4; ++i) cur[i] = nxt[i];
+  }
+  __syncthreads();
+  // low-digit histogram of the kept entries whose top digit is t1
+  for (int f = tid; f < total; f += kSelNT) {
+    const uint2 c = f < kSingleListCap ? list[f] : ovf[f];
+    if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
   }
   __syncthreads();
 
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   const int need_ties = K - sh_above1 - sh_above2;
   int32_t* out = a.out_idx + (size_t)b * K;
   const int written = emit_in_order<kSelNT>(
-      [&](int f) { return f < kListCap ? list[f] : ovf[f]; }, total, tau, need_ties, K,
+      [&](int f) { return f < kSingleListCap ? list[f] : ovf[f]; }, total, tau, need_ties, K,
       scan_scratch, [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
   for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
   if (tid == 0) a.out_count[b] = written;

@@ -60,21 +60,23 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Dequantise 16 channels: 8 code bytes (two words) with E4M3 scale byte sc.
+// The hardware converter decodes E2M1 exactly at scale 1.0; the product with
+// the E4M3 scale (<= 5 significant bits in total) is exact in f16.
 __device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, uint32_t sc, half8& lo,
                                           half8& hi) {
   const _Float16 s = (_Float16)e4m3_value(sc & 0x7Fu);
   const half2v s2 = {s, s};
-  half2v r[8];
-  r[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2;
-  r[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2;
-  r[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * s2;
-  r[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * s2;
-  r[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * s2;
-  r[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * s2;
-  r[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * s2;
-  r[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * s2;
-  lo = half8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-  hi = half8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};
+  uint4 u0, u1;
+  u0.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2);
+  u0.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2);
+  u0.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * s2);
+  u0.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * s2);
+  u1.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * s2);
+  u1.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * s2);
+  u1.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * s2);
+  u1.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * s2);
+  lo = __builtin_bit_cast(half8, u0);
+  hi = __builtin_bit_cast(half8, u1);
 }
 
 __device__ __forceinline__ half8 bf16x8_to_f16(uint4 v) {
@@ -86,6 +88,27 @@ __device__ __forceinline__ half8 bf16x8_to_f16(uint4 v) {
     o[2 * k + 1] = (_Float16)bf16_to_f32(w[k] >> 16);
   }
   return o;
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one head, the 16 tokens a
+// wave holds), with the gfx950 cross-row swaps instead of LDS permutes.
+__device__ __forceinline__ float max_across_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ uint32_t umax_across_rows(uint32_t v) {
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)a[0], (uint32_t)a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)c[0], (uint32_t)c[1]);
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // One thread's quarter of an FP4 row: D/8 code bytes and D/64 scale bytes.
@@ -101,14 +124,14 @@ struct RowPart {
 template <int D>
 __device__ __forceinline__ void load_row_part(RowPart<D>& r, const uint8_t* pages,
                                               long long rowkey, int page_bytes, int scales_off,
-                                              int g_q) {
+                                              int quarter) {
   const long long rk = rowkey < 0 ? 0 : rowkey;
   const uint8_t* page = pages + (size_t)(rk >> 6) * page_bytes;
   const int row = (int)(rk & 63);
-  const uint4* cp = reinterpret_cast<const uint4*>(page + row * (D / 2) + g_q * (D / 8));
+  const uint4* cp = reinterpret_cast<const uint4*>(page + row * (D / 2) + quarter * (D / 8));
 #pragma unroll
   for (int i = 0; i < D / 128; ++i) r.c[i] = cp[i];
-  const uint8_t* sp = page + scales_off + row * (D / 16) + g_q * (D / 64);
+  const uint8_t* sp = page + scales_off + row * (D / 16) + quarter * (D / 64);
   if constexpr (D == 512) {
     r.s = *reinterpret_cast<const uint2*>(sp);
   } else if constexpr (D == 256) {
@@ -127,25 +150,30 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     const int32_t* __restrict__ idx_count, int K, const uint16_t* __restrict__ swa,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml, int batch, int n_splits, int split_tiles) {
-  constexpr int XS = D + 8;                 // LDS row stride (halfs) of the X tile
+  // X row stride: D halves + 24 (48 bytes), so that rows sit 48 bytes apart
+  // modulo 256: the dequant writes (16 consecutive rows per pass), the QK
+  // reads (16 consecutive rows) and the transposed reads (4 rows x 32 bytes)
+  // all touch distinct banks.
+  constexpr int XS = D + 24;
   constexpr int KQ = D / 32;                // MFMA k-steps over D for QK
   constexpr int NB = D / 64;                // 16-dim blocks per wave for PV
-  constexpr int DQ = D / 4;                 // channels per thread in the gather
+  constexpr int DQ = D / 4;                 // channels per wave in the gather
   __shared__ __attribute__((aligned(16))) _Float16 X[kTile * XS];
   __shared__ __attribute__((aligned(16))) _Float16 Pt[kHG * kPStride];
-  __shared__ float red_max[4][kHG];
+  __shared__ __attribute__((aligned(16))) float red_max[kHG][4];
   __shared__ float red_sum[4][kHG];
-  __shared__ uint8_t valid[kTile];
   __shared__ int pt_lds[PTC ? kPtCache : 1];
 
-  // ---- block -> (unit = (sequence, head group), split); a unit's splits share an XCD
+  // ---- block -> (group = (sequence, split), head group); the head groups of
+  // a group share an XCD, so all but the first read its rows from L2
   const int n_hg = H / kHG;
-  const int units = batch * n_hg;
+  const int groups = batch * n_splits;
   const int xcd = blockIdx.x & 7, r8 = blockIdx.x >> 3;
-  const int unit = xcd + 8 * (r8 / n_splits);
-  const int split = r8 % n_splits;
-  if (unit >= units) return;
-  const int b = unit / n_hg, hg = unit % n_hg;
+  const int hg = r8 % n_hg;
+  const int grp = (r8 / n_hg) * 8 + xcd;
+  if (grp >= groups) return;
+  const int b = grp / n_splits, split = grp % n_splits;
+  const int unit = b * n_hg + hg;
 
   int L = ctx_len[b];
   L = L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
@@ -153,20 +181,28 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   int cnt = idx_count[b];
   cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
   const int n_win = L < kWindow ? L : kWindow;
-  // the sequence's tiles: [window 0, window 1, FP4 0, FP4 1, ...]
-  const int tf_plan = (K + kTile - 1) / kTile;
-  const int t_begin = split * split_tiles;
-  const int t_end = min(t_begin + split_tiles, kWinTiles + tf_plan);
+  // The sequence's tiles: two of window rows, then ceil(K/64) of selected
+  // FP4 rows.  With one split a block takes them all; with several, splits 0
+  // and 1 take one window tile each and split s >= 2 takes FP4 tiles
+  // [(s-2)*split_tiles, (s-1)*split_tiles).
   const int tw = (n_win + kTile - 1) / kTile;            // window tiles holding tokens
   const int tf = (cnt + kTile - 1) / kTile;              // FP4 tiles holding tokens
-  const int wa = t_begin, wb = min(t_end, tw);           // this block's window tiles
-  const int fa = max(t_begin - kWinTiles, 0);            // this block's FP4 tiles [fa, fb)
-  const int fb = min(t_end - kWinTiles, tf);
+  int wa = 0, wb = 0, fa = 0, fb = 0;                    // this block's tiles
+  if (n_splits == 1) {
+    wb = tw;
+    fb = tf;
+  } else if (split < kWinTiles) {
+    wa = split;
+    wb = min(split + 1, tw);
+  } else {
+    fa = (split - kWinTiles) * split_tiles;
+    fb = min(fa + split_tiles, tf);
+  }
+  const int nf = fb > fa ? fb - fa : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
-  const int g_tok = tid >> 2;            // gather: token of the tile
-  const int g_q = tid & 3;               // gather: quarter of the channels
+  // gather: lane = token of the tile, wave = quarter of the channels
 
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const int32_t* idx_row = idx + (size_t)b * K;
@@ -176,9 +212,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   // window rows of the first window tile (token k of the window is position L - n_win + k)
   uint4 wreg[DQ / 8];
   auto load_win = [&](int t) {
-    const int k = t * kTile + g_tok;
+    const int k = t * kTile + lane;
     const int p = L - n_win + (k < n_win ? k : 0);
-    const uint4* src = reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + g_q * DQ);
+    const uint4* src =
+        reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + wave * DQ);
 #pragma unroll
     for (int i = 0; i < DQ / 8; ++i) wreg[i] = src[i];
   };
@@ -188,10 +225,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   // computed without it, so that no load result is consumed in the stage
   // that issues it.
   auto pos_load = [&](int f) -> int {
-    const int j = f * kTile + g_tok;
+    const int j = f * kTile + lane;
     return idx_row[j < cnt ? j : cnt - 1];
   };
-  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + g_tok < cnt; };
+  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + lane < cnt; };
   int p0 = -1, p1 = -1, p2 = -1, p3 = -1;
   bool ok3 = false;
   if (fa < fb) {
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i) {
       const int e = i * kBlock + tid;
-      ptv[i] = pt[e < max_pages ? e : 0];
+      if (i * kBlock < max_pages) ptv[i] = pt[e < max_pages ? e : 0];
     }
   }
 
@@ -222,8 +259,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) qmax = max(qmax, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
   }
-  qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 16, 64));
-  qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32, 64));
+  qmax = umax_across_rows(qmax);
   int qexp = 0;
   if (qmax != 0u) {
     int ex;
@@ -244,7 +280,8 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   const float scale2 = ldexpf(scale, -qexp) * kLog2e;
   if (PTC && fa < fb) {
 #pragma unroll
-    for (int i = 0; i < kPtCache / kBlock; ++i) pt_lds[i * kBlock + tid] = ptv[i];
+    for (int i = 0; i < kPtCache / kBlock; ++i)
+      if (i * kBlock < max_pages) pt_lds[i * kBlock + tid] = ptv[i];
   }
   __syncthreads();
 
@@ -269,19 +306,18 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     pg2 = page_of(p2);
     rk0 = rowkey_of(p0, pg0);
     rk1 = rowkey_of(p1, pg1);
-    load_row_part<D>(cur, pages, rk0, page_bytes, scales_off, g_q);
+    load_row_part<D>(cur, pages, rk0, page_bytes, scales_off, wave);
   }
 
-  // running softmax state: per lane for head lc (QK layout) and for heads
-  // 4lg+i (PV layout); identical inputs give identical values in both.
+  // running softmax state of head lc (every lane of the head holds the same);
+  // acc[nb] holds O^T[dims wave*DQ + 16nb + 4lg + i][head lc]
   float m_q = -INFINITY, l_q = 0.0f;
-  float m_o[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   floatx4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- one tile that sits in X (valid[] marks real tokens)
-  auto compute_tile = [&]() {
+  // ---- one tile that sits in X; bit t of `valid` marks token t as real
+  auto compute_tile = [&](uint64_t valid) {
     // S^T for tokens 16*wave .. +16 of the tile, all 16 heads
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
     const _Float16* xa = X + (wave * 16 + lc) * XS + lg * 8;
@@ -290,157 +326,143 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
       const half8 a = *reinterpret_cast<const half8*>(xa + kk * 32);
       s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[kk], s, 0, 0, 0);
     }
+    const uint32_t vbits = (uint32_t)(valid >> (wave * 16 + lg * 4)) & 0xFu;
     float lmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tt = wave * 16 + lg * 4 + i;
-      s[i] = valid[tt] ? s[i] * scale2 : -INFINITY;
+      s[i] = ((vbits >> i) & 1u) ? s[i] * scale2 : -INFINITY;
       lmax = fmaxf(lmax, s[i]);
     }
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-    if (lg == 0) red_max[wave][lc] = lmax;
+    lmax = max_across_rows(lmax);
+    if (lg == 0) red_max[lc][wave] = lmax;
     __syncthreads();
 
-    // online softmax
-    {
-      const float mt =
-          fmaxf(fmaxf(red_max[0][lc], red_max[1][lc]), fmaxf(red_max[2][lc], red_max[3][lc]));
-      const float m_new = fmaxf(m_q, mt);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = exp2f(m_q - m_use);
-      float psum = 0.f;
-      half4 ph;
+    // online softmax of head lc
+    const float4 rm = *reinterpret_cast<const float4*>(&red_max[lc][0]);
+    const float mt = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
+    const float m_new = fmaxf(m_q, mt);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = exp2f(m_q - m_use);
+    float psum = 0.f;
+    half4 ph;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(s[i] - m_use);
-        const _Float16 p16 = (_Float16)pv;
-        ph[i] = p16;
-        psum += (float)p16;             // the weights the PV product actually uses
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_q = l_q * alpha + psum;
-      m_q = m_new;
-      *reinterpret_cast<half4*>(Pt + lc * kPStride + wave * 16 + lg * 4) = ph;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = lg * 4 + i;
-        const float mt_o =
-            fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-        const float mn = fmaxf(m_o[i], mt_o);
-        const float mu = mn == -INFINITY ? 0.0f : mn;
-        const float al = exp2f(m_o[i] - mu);
-        m_o[i] = mn;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb][i] *= al;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 p16 = (_Float16)exp2f(s[i] - m_use);
+      ph[i] = p16;
+      psum += (float)p16;               // the weights the PV product actually uses
     }
+    l_q = l_q * alpha + sum_across_rows(psum);
+    m_q = m_new;
+    *reinterpret_cast<half4*>(Pt + lc * kPStride + wave * 16 + lg * 4) = ph;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
     __syncthreads();
 
-    // O[16 heads][wave's D/4] += P X
+    // O^T[wave's D/4 dims][16 heads] += X^T P^T
 #pragma unroll
     for (int kb = 0; kb < kTile / 32; ++kb) {
-      const half8 a = *reinterpret_cast<const half8*>(Pt + lc * kPStride + kb * 32 + lg * 8);
+      const half8 pb = *reinterpret_cast<const half8*>(Pt + lc * kPStride + kb * 32 + lg * 8);
       const int tok0 = kb * 32 + lg * 8 + (lc >> 2);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = wave * DQ + nb * 16 + 4 * (lc & 3);
         const half4 b0 = lds_read_tr(X + tok0 * XS + col);
         const half4 b1 = lds_read_tr(X + (tok0 + 4) * XS + col);
-        const half8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, acc[nb], 0, 0, 0);
+        const half8 xt = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xt, pb, acc[nb], 0, 0, 0);
       }
     }
     __syncthreads();
   };
 
-  _Float16* xrow = X + g_tok * XS + g_q * DQ;
+  _Float16* xrow = X + lane * XS + wave * DQ;
 
   // ---- window tiles (their rows were requested in the prologue)
 #pragma unroll 1
   for (int t = wa; t < wb; ++t) {
-    const bool ok = t * kTile + g_tok < n_win;
+    const bool ok = t * kTile + lane < n_win;
 #pragma unroll
     for (int i = 0; i < DQ / 8; ++i)
       *reinterpret_cast<half8*>(xrow + 8 * i) = ok ? bf16x8_to_f16(wreg[i]) : half8{};
-    if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
+    const uint64_t valid = __ballot(ok);
     if (t + 1 < wb) load_win(t + 1);    // in flight while this tile computes
     __syncthreads();
-    compute_tile();
+    compute_tile(valid);
   }
 
-  // ---- FP4 tiles: a pipeline position -> page -> row address -> rows, so
-  // that tile f computes while the rows of f+1, the page of f+3 and the
-  // position of f+4 are on their way
-#pragma unroll 1
-  for (int f = fa; f < fb; ++f) {
-    load_row_part<D>(nxt, pages, rk1, page_bytes, scales_off, g_q);
-    const long long rk2 = rowkey_of(p2, pg2);
-    const int pg3 = page_of(ok3 ? p3 : -1);
-    const int p4 = pos_load(f + 4);          // consumed next iteration
-    const bool ok4 = pos_ok(f + 4);
-    const bool ok = rk0 >= 0;
+  // ---- FP4 tiles
+  auto fp4_tile = [&](const RowPart<D>& rp, long long rk) {
+    const bool ok = rk >= 0;
 #pragma unroll
     for (int g = 0; g < DQ / 16; ++g) {
-      const uint4 c4 = cur.c[g / 2];
+      const uint4 c4 = rp.c[g / 2];
       const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
-      const uint32_t sc = ((g < 4 ? cur.s.x : cur.s.y) >> (8 * (g & 3))) & 0xFFu;
+      const uint32_t sc = ((g < 4 ? rp.s.x : rp.s.y) >> (8 * (g & 3))) & 0xFFu;
       half8 lo, hi;
       dequant16(w0, w1, sc, lo, hi);
       *reinterpret_cast<half8*>(xrow + 16 * g) = ok ? lo : half8{};
       *reinterpret_cast<half8*>(xrow + 16 * g + 8) = ok ? hi : half8{};
     }
-    if (g_q == 0) valid[g_tok] = ok ? 1 : 0;
+    const uint64_t valid = __ballot(ok);
     __syncthreads();
-    compute_tile();
-    rk0 = rk1;
-    rk1 = rk2;
-    p2 = ok3 ? p3 : -1;
-    pg2 = pg3;
-    p3 = p4;
-    ok3 = ok4;
-    cur = nxt;
+    compute_tile(valid);
+  };
+  if (nf > 0 && nf <= 4) {
+    // a short run: every row of the run is requested at once
+    const long long rk3 = rowkey_of(ok3 ? p3 : -1, page_of(ok3 ? p3 : -1));
+    const long long rk2 = rowkey_of(p2, pg2);
+    RowPart<D> r1, r2, r3;
+    if (nf > 1) load_row_part<D>(r1, pages, rk1, page_bytes, scales_off, wave);
+    if (nf > 2) load_row_part<D>(r2, pages, rk2, page_bytes, scales_off, wave);
+    if (nf > 3) load_row_part<D>(r3, pages, rk3, page_bytes, scales_off, wave);
+    fp4_tile(cur, rk0);
+    if (nf > 1) fp4_tile(r1, rk1);
+    if (nf > 2) fp4_tile(r2, rk2);
+    if (nf > 3) fp4_tile(r3, rk3);
+  } else {
+    // a long run: a pipeline position -> page -> row address -> rows, so that
+    // tile f computes while the rows of f+1, the page of f+3 and the position
+    // of f+4 are on their way
+#pragma unroll 1
+    for (int f = fa; f < fb; ++f) {
+      load_row_part<D>(nxt, pages, rk1, page_bytes, scales_off, wave);
+      const long long rk2 = rowkey_of(p2, pg2);
+      const int pg3 = page_of(ok3 ? p3 : -1);
+      const int p4 = pos_load(f + 4);          // consumed next iteration
+      const bool ok4 = pos_ok(f + 4);
+      fp4_tile(cur, rk0);
+      rk0 = rk1;
+      rk1 = rk2;
+      p2 = ok3 ? p3 : -1;
+      pg2 = pg3;
+      p3 = p4;
+      ok3 = ok4;
+      cur = nxt;
+    }
   }
 
-  // ---- finish: total l per head across waves (every wave saw the same m)
+  // ---- finish: total l of head lc across waves (every wave saw the same m)
   if (lg == 0) red_sum[wave][lc] = l_q;
   __syncthreads();
-  float l_o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = lg * 4 + i;
-    l_o[i] = red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h];
-  }
+  const float l_tot = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
+  const int head = hg * kHG + lc;
   if (n_splits == 1) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.0f;
+    float* orow = out + ((size_t)b * H + head) * D + wave * DQ + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = hg * kHG + lg * 4 + i;
-      const float inv = l_o[i] > 0.f ? 1.0f / l_o[i] : 0.0f;
-      float* orow = out + ((size_t)b * H + head) * D + wave * DQ + lc;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) orow[nb * 16] = acc[nb][i] * inv;
-    }
-    if (wave == 0 && lg == 0 && lse != nullptr) {
-      const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
-      lse[(size_t)b * H + hg * kHG + lc] = lt > 0.f ? (m_q + log2f(lt)) * kLn2 : -INFINITY;
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<floatx4*>(orow + nb * 16) = acc[nb] * inv;
+    if (wave == 0 && lg == 0 && lse != nullptr)
+      lse[(size_t)b * H + head] = l_tot > 0.f ? (m_q + log2f(l_tot)) * kLn2 : -INFINITY;
     return;
   }
 
   // ---- split partials: (m, l) per head and the unnormalised O
-  const size_t ubase = (size_t)unit * n_splits;          // partial rows of this unit
+  const size_t prow = ((size_t)unit * n_splits + split) * kHG + lc;   // partial row of head lc
+  float* orow = part_o + prow * D + wave * DQ + 4 * lg;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = lg * 4 + i;
-    float* orow = part_o + ((ubase + split) * kHG + h) * D + wave * DQ + lc;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) orow[nb * 16] = acc[nb][i];
-  }
-  if (wave == 0 && lg == 0) {
-    const float lt = red_sum[0][lc] + red_sum[1][lc] + red_sum[2][lc] + red_sum[3][lc];
-    part_ml[(ubase + split) * kHG + lc] = make_float2(m_q, lt);
-  }
+  for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<floatx4*>(orow + nb * 16) = acc[nb];
+  if (wave == 0 && lg == 0) part_ml[prow] = make_float2(m_q, l_tot);
 }
 
 // LSE merge of the split partials.  Block = (unit, HPB heads); thread = one
@@ -514,18 +536,22 @@ struct DecodePlan {
 #define CSA2_DECODE_MIN_SPLIT_TILES 3
 #endif
 
-// Splits so that the grid stays within one resident wave of blocks (two per
-// CU on 256 CUs), with at least CSA2_DECODE_MIN_SPLIT_TILES tiles per split
-// so that the partials stay small next to the work, and at most kMaxSplits.
+// Splits: with at least 256 (sequence, head group) units one block per unit
+// takes all of a sequence's tiles.  Otherwise two one-tile splits take the window tiles
+// and FP4 runs of split_tiles tiles fill the rest, enough of them to keep the
+// grid near one resident wave of blocks (two per CU on 256 CUs) but at least
+// CSA2_DECODE_MIN_SPLIT_TILES tiles per run, so that the partials stay small
+// next to the work, and at most kMaxSplits splits.
 static DecodePlan plan_decode(int batch, int H, int K) {
-  const int tiles = (K + kTile - 1) / kTile + kWinTiles;
+  const int tiles = (K + kTile - 1) / kTile;             // FP4 tiles
   const int units = batch * (H / kHG);
+  if (units >= 256 || tiles == 0) return DecodePlan{1, tiles + kWinTiles};
   int tps = (tiles * units + 511) / 512;
   if (tps < CSA2_DECODE_MIN_SPLIT_TILES) tps = CSA2_DECODE_MIN_SPLIT_TILES;
-  const int min_tps = (tiles + kMaxSplits - 1) / kMaxSplits;
+  const int min_tps = (tiles + kMaxSplits - kWinTiles - 1) / (kMaxSplits - kWinTiles);
   if (tps < min_tps) tps = min_tps;
   if (tps > tiles) tps = tiles;
-  return DecodePlan{(tiles + tps - 1) / tps, tps};
+  return DecodePlan{kWinTiles + (tiles + tps - 1) / tps, tps};
 }
 
 struct DecodeWs {
@@ -556,7 +582,8 @@ static void launch_decode(const CacheArgs& c, const int32_t* ctx_len, int H, con
   const DecodePlan pl = plan_decode(c.batch, H, K);
   const DecodeWs w = decode_ws(c.batch, H, D, K);
   const int units = c.batch * (H / kHG);
-  const int blocks = ((units + 7) / 8) * 8 * pl.n_splits;
+  const int groups = c.batch * pl.n_splits;
+  const int blocks = ((groups + 7) / 8) * 8 * (H / kHG);
   auto kern = c.max_pages <= kPtCache ? sparse_decode_kernel<D, true>
                                       : sparse_decode_kernel<D, false>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBlock), 0, st, (const uint8_t*)c.pages,
