@@ -151,17 +151,20 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml, int batch, int n_splits, int split_tiles) {
   // X row stride: D halves + 24 (48 bytes), so that rows sit 48 bytes apart
-  // modulo 256: the dequant writes (16 consecutive rows per pass), the QK
-  // reads (16 consecutive rows) and the transposed reads (4 rows x 32 bytes)
-  // all touch distinct banks.
+  // modulo 256: the dequant writes (16 consecutive rows per 16 lanes) and the
+  // transposed reads (4 rows x 32 bytes) touch distinct banks.
   constexpr int XS = D + 24;
+  constexpr int QS = D + 8;                 // row stride of the staged queries
   constexpr int KQ = D / 32;                // MFMA k-steps over D for QK
   constexpr int NB = D / 64;                // 16-dim blocks per wave for PV
-  constexpr int DQ = D / 4;                 // channels per wave in the gather
+  constexpr int DQ = D / 4;                 // channels per lane in the gather
+  constexpr int QPL = D / 16 / 8;           // uint4 of one head's query per lane in staging
+  static_assert(kHG * QS <= kTile * XS, "query staging fits in the X tile");
   __shared__ __attribute__((aligned(16))) _Float16 X[kTile * XS];
   __shared__ __attribute__((aligned(16))) _Float16 Pt[kHG * kPStride];
   __shared__ __attribute__((aligned(16))) float red_max[kHG][4];
   __shared__ float red_sum[4][kHG];
+  __shared__ int q_exp[kHG];
   __shared__ int pt_lds[PTC ? kPtCache : 1];
 
   // ---- block -> (group = (sequence, split), head group); the head groups of
@@ -202,7 +205,9 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
-  // gather: lane = token of the tile, wave = quarter of the channels
+  // gather: lane (lc, lg) of wave w holds token 16w + lc of the tile,
+  // channels [lg*D/4, (lg+1)*D/4)
+  const int tok = wave * 16 + lc;
 
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const int32_t* idx_row = idx + (size_t)b * K;
@@ -212,10 +217,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   // window rows of the first window tile (token k of the window is position L - n_win + k)
   uint4 wreg[DQ / 8];
   auto load_win = [&](int t) {
-    const int k = t * kTile + lane;
+    const int k = t * kTile + tok;
     const int p = L - n_win + (k < n_win ? k : 0);
     const uint4* src =
-        reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + wave * DQ);
+        reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + lg * DQ);
 #pragma unroll
     for (int i = 0; i < DQ / 8; ++i) wreg[i] = src[i];
   };
@@ -225,10 +230,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   // computed without it, so that no load result is consumed in the stage
   // that issues it.
   auto pos_load = [&](int f) -> int {
-    const int j = f * kTile + lane;
+    const int j = f * kTile + tok;
     return idx_row[j < cnt ? j : cnt - 1];
   };
-  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + lane < cnt; };
+  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + tok < cnt; };
   int p0 = -1, p1 = -1, p2 = -1, p3 = -1;
   bool ok3 = false;
   if (fa < fb) {
@@ -247,43 +252,62 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     }
   }
 
-  // ---- queries: lane holds head lc, dims 32kk + 8lg .. +8, as exact f16 of q*2^e
-  const int head_q = hg * kHG + lc;
-  const uint16_t* qrow = q + ((size_t)b * H + head_q) * D;
-  uint4 qraw[KQ];
-  uint32_t qmax = 0;
+  // ---- queries, staged once per block: wave w converts heads 4w .. 4w+3
+  // (16 lanes per head) to exact f16 copies of q * 2^e, e chosen per head so
+  // that the largest |q| lands in [2^14, 2^15); the staging aliases X
+  _Float16* Qs = X;
+  {
+    const int hq = wave * 4 + lg;                        // head within the group
+    const uint16_t* src = q + ((size_t)b * H + hg * kHG + hq) * D + lc * (D / 16);
+    uint4 qraw[QPL];
+    uint32_t qmax = 0;
 #pragma unroll
-  for (int kk = 0; kk < KQ; ++kk) {
-    qraw[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 32 + lg * 8);
-    const uint32_t w[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
+    for (int i = 0; i < QPL; ++i) {
+      qraw[i] = reinterpret_cast<const uint4*>(src)[i];
+      const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qmax = max(qmax, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
-  }
-  qmax = umax_across_rows(qmax);
-  int qexp = 0;
-  if (qmax != 0u) {
-    int ex;
-    frexpf(bf16_to_f32(qmax), &ex);     // max|q| in [2^(ex-1), 2^ex)
-    qexp = 15 - ex;                     // scaled max in [2^14, 2^15)
-  }
-  half8 qf[KQ];
+      for (int k = 0; k < 4; ++k) qmax = max(qmax, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
 #pragma unroll
-  for (int kk = 0; kk < KQ; ++kk) {
-    const uint32_t w[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
+    for (int m = 8; m >= 1; m >>= 1) qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, m, 16));
+    int qexp = 0;
+    if (qmax != 0u) {
+      int ex;
+      frexpf(bf16_to_f32(qmax), &ex);     // max|q| in [2^(ex-1), 2^ex)
+      qexp = 15 - ex;
+    }
+    if (lc == 0) q_exp[hq] = qexp;
+    _Float16* dst = Qs + hq * QS + lc * (D / 16);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      qf[kk][2 * k] = (_Float16)ldexpf(bf16_to_f32(w[k] & 0xFFFFu), qexp);
-      qf[kk][2 * k + 1] = (_Float16)ldexpf(bf16_to_f32(w[k] >> 16), qexp);
+    for (int i = 0; i < QPL; ++i) {
+      const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+      half8 h;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[2 * k] = (_Float16)ldexpf(bf16_to_f32(w[k] & 0xFFFFu), qexp);
+        h[2 * k + 1] = (_Float16)ldexpf(bf16_to_f32(w[k] >> 16), qexp);
+      }
+      *reinterpret_cast<half8*>(dst + 8 * i) = h;
     }
   }
-  // logits in log2 units: scale2 * (q~ . x)
-  const float scale2 = ldexpf(scale, -qexp) * kLog2e;
   if (PTC && fa < fb) {
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i)
       if (i * kBlock < max_pages) pt_lds[i * kBlock + tid] = ptv[i];
   }
   __syncthreads();
+  // QK operands.  The contraction over D may visit the channels in any order
+  // as long as X and Q agree: k-step kk takes, in lane row lg, channels
+  // lg*D/4 + 8kk .. +8, which are exactly the channels a gather lane holds,
+  // so the X operand comes straight from the dequantised registers.
+  // qf[kk]: head lc, channels lg*D/4 + 8kk .. +8.
+  half8 qf[KQ];
+#pragma unroll
+  for (int kk = 0; kk < KQ; ++kk)
+    qf[kk] = *reinterpret_cast<const half8*>(Qs + lc * QS + lg * DQ + 8 * kk);
+  // logits in log2 units: scale2 * (q~ . x) for head lc
+  const float scale2 = ldexpf(scale, -q_exp[lc]) * kLog2e;
+  __syncthreads();                      // the staging area becomes the X tile
 
   // page of a selected position (-1 if it is not a selectable position)
   auto page_of = [&](int p) -> int {
@@ -306,7 +330,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     pg2 = page_of(p2);
     rk0 = rowkey_of(p0, pg0);
     rk1 = rowkey_of(p1, pg1);
-    load_row_part<D>(cur, pages, rk0, page_bytes, scales_off, wave);
+    load_row_part<D>(cur, pages, rk0, page_bytes, scales_off, lg);
   }
 
   // running softmax state of head lc (every lane of the head holds the same);
@@ -316,17 +340,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- one tile that sits in X; bit t of `valid` marks token t as real
-  auto compute_tile = [&](uint64_t valid) {
-    // S^T for tokens 16*wave .. +16 of the tile, all 16 heads
-    floatx4 s = {0.f, 0.f, 0.f, 0.f};
-    const _Float16* xa = X + (wave * 16 + lc) * XS + lg * 8;
-#pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) {
-      const half8 a = *reinterpret_cast<const half8*>(xa + kk * 32);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[kk], s, 0, 0, 0);
-    }
-    const uint32_t vbits = (uint32_t)(valid >> (wave * 16 + lg * 4)) & 0xFu;
+  // ---- the rest of a tile once this wave's S^T (tokens 16*wave + 4lg + i,
+  // head lc) is known and the tile's rows are being written to X; bit i of
+  // vbits marks token 16*wave + 4lg + i as real
+  auto finish_tile = [&](floatx4 s, uint32_t vbits) {
     float lmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -335,7 +352,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     }
     lmax = max_across_rows(lmax);
     if (lg == 0) red_max[lc][wave] = lmax;
-    __syncthreads();
+    __syncthreads();                    // also: the whole X tile is written
 
     // online softmax of head lc
     const float4 rm = *reinterpret_cast<const float4*>(&red_max[lc][0]);
@@ -375,24 +392,29 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     __syncthreads();
   };
 
-  _Float16* xrow = X + lane * XS + wave * DQ;
+  _Float16* xrow = X + tok * XS + lg * DQ;
 
   // ---- window tiles (their rows were requested in the prologue)
 #pragma unroll 1
   for (int t = wa; t < wb; ++t) {
-    const bool ok = t * kTile + lane < n_win;
+    const bool ok = t * kTile + tok < n_win;
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < DQ / 8; ++i)
-      *reinterpret_cast<half8*>(xrow + 8 * i) = ok ? bf16x8_to_f16(wreg[i]) : half8{};
-    const uint64_t valid = __ballot(ok);
+    for (int kk = 0; kk < KQ; ++kk) {
+      const half8 x = ok ? bf16x8_to_f16(wreg[kk]) : half8{};
+      *reinterpret_cast<half8*>(xrow + 8 * kk) = x;
+      if (kk & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, qf[kk], s1, 0, 0, 0);
+      else        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, qf[kk], s0, 0, 0, 0);
+    }
+    const uint32_t vbits = (uint32_t)(__ballot(ok) >> (4 * lg)) & 0xFu;
     if (t + 1 < wb) load_win(t + 1);    // in flight while this tile computes
-    __syncthreads();
-    compute_tile(valid);
+    finish_tile(s0 + s1, vbits);
   }
 
   // ---- FP4 tiles
   auto fp4_tile = [&](const RowPart<D>& rp, long long rk) {
     const bool ok = rk >= 0;
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < DQ / 16; ++g) {
       const uint4 c4 = rp.c[g / 2];
@@ -400,21 +422,24 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
       const uint32_t sc = ((g < 4 ? rp.s.x : rp.s.y) >> (8 * (g & 3))) & 0xFFu;
       half8 lo, hi;
       dequant16(w0, w1, sc, lo, hi);
-      *reinterpret_cast<half8*>(xrow + 16 * g) = ok ? lo : half8{};
-      *reinterpret_cast<half8*>(xrow + 16 * g + 8) = ok ? hi : half8{};
+      lo = ok ? lo : half8{};
+      hi = ok ? hi : half8{};
+      *reinterpret_cast<half8*>(xrow + 16 * g) = lo;
+      *reinterpret_cast<half8*>(xrow + 16 * g + 8) = hi;
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qf[2 * g], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf[2 * g + 1], s1, 0, 0, 0);
     }
-    const uint64_t valid = __ballot(ok);
-    __syncthreads();
-    compute_tile(valid);
+    const uint32_t vbits = (uint32_t)(__ballot(ok) >> (4 * lg)) & 0xFu;
+    finish_tile(s0 + s1, vbits);
   };
   if (nf > 0 && nf <= 4) {
     // a short run: every row of the run is requested at once
     const long long rk3 = rowkey_of(ok3 ? p3 : -1, page_of(ok3 ? p3 : -1));
     const long long rk2 = rowkey_of(p2, pg2);
     RowPart<D> r1, r2, r3;
-    if (nf > 1) load_row_part<D>(r1, pages, rk1, page_bytes, scales_off, wave);
-    if (nf > 2) load_row_part<D>(r2, pages, rk2, page_bytes, scales_off, wave);
-    if (nf > 3) load_row_part<D>(r3, pages, rk3, page_bytes, scales_off, wave);
+    if (nf > 1) load_row_part<D>(r1, pages, rk1, page_bytes, scales_off, lg);
+    if (nf > 2) load_row_part<D>(r2, pages, rk2, page_bytes, scales_off, lg);
+    if (nf > 3) load_row_part<D>(r3, pages, rk3, page_bytes, scales_off, lg);
     fp4_tile(cur, rk0);
     if (nf > 1) fp4_tile(r1, rk1);
     if (nf > 2) fp4_tile(r2, rk2);
@@ -425,7 +450,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     // of f+4 are on their way
 #pragma unroll 1
     for (int f = fa; f < fb; ++f) {
-      load_row_part<D>(nxt, pages, rk1, page_bytes, scales_off, wave);
+      load_row_part<D>(nxt, pages, rk1, page_bytes, scales_off, lg);
       const long long rk2 = rowkey_of(p2, pg2);
       const int pg3 = page_of(ok3 ? p3 : -1);
       const int p4 = pos_load(f + 4);          // consumed next iteration
