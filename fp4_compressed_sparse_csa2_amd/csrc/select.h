@@ -78,51 +78,62 @@ __device__ void find_digit(const HistT* hist, int need, int* scan_scratch, int* 
   find_digit_in<NT>(load_digit_bins<NT>(hist), need, scan_scratch, t_out, above_out);
 }
 
-constexpr int kEmitPerThread = 8;   // entries per thread per round of the emission
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // Emit the selection from candidates that arrive in ascending id order.
 //   get(f) -> uint2{key, id} for f < total, ids strictly ascending in f.
 //   key > tau: selected; key == tau: the first `need_ties` of them (lowest
 //   ids) are selected; key < tau: dropped.
 // Calls put(j, id) for the j-th selected entry (ascending ids), j < K, and
-// returns the number selected (uniform).  `scan_scratch`: NT/64 shared ints.
-// All threads must call.
-template <int NT = kBlock, typename Get, typename Put>
+// returns the number selected (uniform).  Each wave takes one contiguous run
+// of candidates, counts its selections with ballots, and after one barrier
+// (the per-wave totals, `wave_tot`: NT/64 shared int2) places them with
+// in-wave prefix counts.  All threads must call, once per kernel.
+template <int NT, typename Get, typename Put>
 __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, int K,
-                             int* scan_scratch, Put put) {
-  constexpr int E = kEmitPerThread;
-  int carry_gt = 0, carry_tie = 0;
-  for (int base = 0; base < total; base += NT * E) {
-    const int f0 = base + (int)threadIdx.x * E;
-    uint2 c[E];
-    int n_gt = 0, n_tie = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      c[e] = (f0 + e < total) ? get(f0 + e) : make_uint2(0u, 0u);
-      const bool live = f0 + e < total;
-      n_gt += (live && c[e].x > tau) ? 1 : 0;
-      n_tie += (live && c[e].x == tau) ? 1 : 0;
-    }
-    // one scan carries both counts: per round each is <= NT * E < 2^16
-    int round_total;
-    const int pre = block_exclusive_scan<NT>(n_gt | (n_tie << 16), scan_scratch, &round_total);
-    int g = carry_gt + (pre & 0xFFFF), t = carry_tie + (pre >> 16);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (f0 + e >= total) break;
-      if (c[e].x > tau) {
-        const int slot = g + (t < need_ties ? t : need_ties);
-        if (slot < K) put(slot, c[e].y);
-        ++g;
-      } else if (c[e].x == tau) {
-        if (t < need_ties && g + t < K) put(g + t, c[e].y);
-        ++t;
-      }
-    }
-    carry_gt += round_total & 0xFFFF;
-    carry_tie += round_total >> 16;
+                             int2* wave_tot, Put put) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int run = ((total + NT - 1) / NT) * 64;          // a multiple of 64 per wave
+  const int f0 = wave * run;
+  const int f1 = min(f0 + run, total);
+  int g = 0, t = 0;
+  for (int f = f0 + lane; f - lane < f1; f += 64) {      // wave-uniform trip count
+    const bool live = f < f1;
+    const uint32_t key = live ? get(f).x : 0u;
+    g += __popcll(__ballot(live && key > tau));
+    t += __popcll(__ballot(live && key == tau));
   }
-  const int n = carry_gt + (carry_tie < need_ties ? carry_tie : need_ties);
+  if (lane == 0) wave_tot[wave] = make_int2(g, t);
+  __syncthreads();
+  int g0 = 0, t0 = 0, G = 0, T = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int2 v = wave_tot[w];
+    g0 += w < wave ? v.x : 0;
+    t0 += w < wave ? v.y : 0;
+    G += v.x;
+    T += v.y;
+  }
+  for (int f = f0 + lane; f - lane < f1; f += 64) {
+    const bool live = f < f1;
+    const uint2 c = live ? get(f) : make_uint2(0u, 0u);
+    const bool gt = live && c.x > tau, tie = live && c.x == tau;
+    const uint64_t bg = __ballot(gt), bt = __ballot(tie);
+    const int gb = g0 + lanes_below(bg), tb = t0 + lanes_below(bt);   // before this entry
+    if (gt) {
+      const int slot = gb + (tb < need_ties ? tb : need_ties);
+      if (slot < K) put(slot, c.y);
+    } else if (tie) {
+      if (tb < need_ties && gb + tb < K) put(gb + tb, c.y);
+    }
+    g0 += __popcll(bg);
+    t0 += __popcll(bt);
+  }
+  const int n = G + (T < need_ties ? T : need_ties);
   return n < K ? n : K;
 }
 

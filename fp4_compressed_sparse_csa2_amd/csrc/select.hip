@@ -13,11 +13,13 @@
 // cross-block synchronisation inside a kernel (visibility comes from kernel
 // boundaries):
 //   single  - up to kSingleMax entries: one block per sequence finds the
-//             K-th largest top digit t1, reads the scores once (every load of
-//             a 32K-entry round in flight together) keeping the entries with
-//             digit >= t1 in entry order (one block scan per round) and
-//             histogramming the low digit of those equal to t1, fixes the
-//             exact threshold and emits in order.
+//             K-th largest top digit t1 and reads the scores once, in rounds
+//             of 16K entries where each wave streams a contiguous run with
+//             1 KB loads (the next round's loads in flight while one is
+//             compacted), keeping the entries with digit >= t1 in entry
+//             order (ballot prefix counts in the wave, one barrier per
+//             round); then it histograms the low digit of the kept entries
+//             equal to t1, fixes the exact threshold and emits in order.
 //   filter  - longer sequences: 4096-entry blocks keep their digit >= t1
 //   + final   entries, in order, in their own slots; then one block per
 //             sequence concatenates the slot lists (already in order),
@@ -29,11 +31,13 @@
 
 namespace csa2 {
 
-constexpr int kSelNT = 512;                      // threads of the one-block-per-sequence kernels
-constexpr int kSelPT = 64;                       // entries per thread per round
-constexpr int kSelRound = kSelNT * kSelPT;       // 32768 entries (128 KB) per round
+constexpr int kSelNT = 1024;                     // threads of the one-block-per-sequence kernels
+constexpr int kSelWaves = kSelNT / 64;
+constexpr int kSelLd = 4;                        // 16-byte loads per lane per round
+constexpr int kWaveRun = 64 * 4 * kSelLd;        // 1024 entries per wave per round
+constexpr int kSelRound = kSelWaves * kWaveRun;  // 16384 entries (64 KB) per round
 constexpr int kListCap = 6144;                   // candidates the final kernel keeps in LDS
-constexpr int kSingleListCap = 2944;             // candidates the single kernel keeps in LDS
+constexpr int kSingleListCap = 6144;             // candidates the single kernel keeps in LDS
 constexpr int kFiltPer = 16;                     // entries per thread in the filter kernel
 constexpr int kFiltChunk = kBlock * kFiltPer;    // 4096 entries per filter block
 
@@ -63,15 +67,17 @@ __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, in
 }
 
 // ------------------------------------------------------------------ single
-// Thread t takes the 64 entries at r * 32768 + 64t of round r; every load of
-// a round (and, for the first, the histogram) is issued before any result is
-// used, so each 32768-entry round costs one memory round trip.
-// The streaming passes touch LDS only to write the (rare) kept entries; the
-// low-digit histogram is built afterwards from the kept list.
+// Round r, wave w streams entries [r*16384 + 1024w, +1024): lane l's load i
+// holds the four entries at 256i + 4l of that run, so every load instruction
+// of a wave reads 1 KB of consecutive scores.  In entry order the kept
+// entries of a wave are ordered by (i, lane, k); a lane's place among them
+// comes from ballots of its per-load counts.
 __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
   __shared__ uint2 list[kSingleListCap];
-  __shared__ int scan_scratch[kSelNT / 64];
+  __shared__ int scan_scratch[kSelWaves];
+  __shared__ int round_tot[2][kSelWaves];
+  __shared__ int2 wave_tot[kSelWaves];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2;
 
   const int b = blockIdx.x;
@@ -81,25 +87,25 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
     select_all(a, b, n, kSelNT);
     return;
   }
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   const int32_t* row = a.scores + (size_t)b * a.stride;
   uint2* ovf = a.cand + (size_t)b * a.stride;
   const int rounds = (n + kSelRound - 1) / kSelRound;
 
-  // Entry indices and the row stride are multiples of 16, so a 16-entry run
-  // that starts below n lies inside the row; runs past n load entry 0.
-  uint4 v[kSelPT / 4];
-  auto load_round = [&](int r) {
+  // Entry indices of a load are multiples of 4 and the row stride a multiple
+  // of 64, so a load that starts below n lies inside the row; loads that
+  // start at or past n read entry 0 instead and are masked.
+  auto load_round = [&](uint4 (&v)[kSelLd], int r) {
+    const int base = r * kSelRound + wave * kWaveRun + 4 * lane;
 #pragma unroll
-    for (int c = 0; c < kSelPT / 16; ++c) {
-      const int q0 = r * kSelRound + tid * kSelPT + 16 * c;
-      const uint4* src = reinterpret_cast<const uint4*>(row + (q0 < n ? q0 : 0));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[4 * c + i] = src[i];
+    for (int i = 0; i < kSelLd; ++i) {
+      const int e0 = base + 256 * i;
+      v[i] = *reinterpret_cast<const uint4*>(row + (e0 < n ? e0 : 0));
     }
   };
-  load_round(0);
+  uint4 va[kSelLd], vb[kSelLd];
+  load_round(va, 0);
   const DigitBins<kSelNT> bins = load_digit_bins<kSelNT>(h1);
   for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
@@ -109,39 +115,69 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   const int lo = sh_t1 < 0 ? INT_MAX : (int)(t1 << 11) - kKeyBias;
 
   int total = 0;
-  for (int r = 0; r < rounds; ++r) {
-    if (r > 0) load_round(r);
-    const int p0 = r * kSelRound + tid * kSelPT;
-    int nk = 0;
+  // kept-entry mask of load i (bit k: entry e0 + k) and its in-wave counts
+  auto keep_mask = [&](const uint4& v, int e0) -> uint32_t {
+    const int w[4] = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < kSelPT / 4; ++i) {
-      const int w[4] = {(int)v[i].x, (int)v[i].y, (int)v[i].z, (int)v[i].w};
+    for (int k = 0; k < 4; ++k) m |= (w[k] >= lo && e0 + k < n) ? (1u << k) : 0u;
+    return m;
+  };
+  auto keep_round = [&](const uint4 (&v)[kSelLd], int r) {
+    const int base = r * kSelRound + wave * kWaveRun + 4 * lane;
+    // pass 1: the wave's number of kept entries
+    int wtot = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) nk += (w[k] >= lo && p0 + 4 * i + k < n) ? 1 : 0;
+    for (int i = 0; i < kSelLd; ++i) {
+      const uint32_t c = __builtin_popcount(keep_mask(v[i], base + 256 * i));
+      wtot += (int)(__popcll(__ballot(c & 1u)) + 2 * __popcll(__ballot(c & 2u)) +
+                    4 * __popcll(__ballot(c & 4u)));
     }
-    int round_total;
-    int slot = total + block_exclusive_scan<kSelNT>(nk, scan_scratch, &round_total);
-    if (nk > 0) {
+    if (lane == 0) round_tot[r & 1][wave] = wtot;
+    __syncthreads();
+    int woff = total, rtot = 0;
 #pragma unroll
-      for (int i = 0; i < kSelPT / 4; ++i) {
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int t = round_tot[r & 1][w];
+      woff += w < wave ? t : 0;
+      rtot += t;
+    }
+    // pass 2: place them in entry order (load i, then lane, then k)
+    if (wtot > 0) {                                     // wave-uniform
+#pragma unroll
+      for (int i = 0; i < kSelLd; ++i) {
+        const int e0 = base + 256 * i;
+        const uint32_t m = keep_mask(v[i], e0);
+        const uint32_t c = __builtin_popcount(m);
+        const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+        int slot = woff + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+        woff += (int)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
         const int w[4] = {(int)v[i].x, (int)v[i].y, (int)v[i].z, (int)v[i].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int p = p0 + 4 * i + k;
-          if (w[k] >= lo && p < n) {
-            const uint2 c = make_uint2(score_key(w[k]), (uint32_t)p);
-            if (slot < kSingleListCap) list[slot] = c; else ovf[slot] = c;
+          if ((m >> k) & 1u) {
+            const uint2 cc = make_uint2(score_key(w[k]), (uint32_t)(e0 + k));
+            if (slot < kSingleListCap) list[slot] = cc; else ovf[slot] = cc;
             ++slot;
           }
         }
       }
     }
-    total += round_total;
+    total += rtot;
+  };
+  // two round buffers: round r + 1 is in flight while round r is compacted
+  for (int r = 0; r < rounds; r += 2) {
+    if (r + 1 < rounds) load_round(vb, r + 1);
+    keep_round(va, r);
+    if (r + 1 >= rounds) break;
+    if (r + 2 < rounds) load_round(va, r + 2);
+    keep_round(vb, r + 1);
   }
   __syncthreads();
+  auto get = [&](int f) -> uint2 { return f < kSingleListCap ? list[f] : ovf[f]; };
   // low-digit histogram of the kept entries whose top digit is t1
   for (int f = tid; f < total; f += kSelNT) {
-    const uint2 c = f < kSingleListCap ? list[f] : ovf[f];
+    const uint2 c = get(f);
     if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
   }
   __syncthreads();
@@ -151,8 +187,8 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   const int need_ties = K - sh_above1 - sh_above2;
   int32_t* out = a.out_idx + (size_t)b * K;
   const int written = emit_in_order<kSelNT>(
-      [&](int f) { return f < kSingleListCap ? list[f] : ovf[f]; }, total, tau, need_ties, K,
-      scan_scratch, [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
+      get, total, tau, need_ties, K, wave_tot,
+      [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
   for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
   if (tid == 0) a.out_count[b] = written;
   for (int i = tid; i < kBins; i += kSelNT) h1[i] = 0u;     // ready for the next call
@@ -204,11 +240,20 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ final
+// Direct plan (at most one chunk per wave): wave w requests the first
+// kSpecPerChunk candidates of chunk w together with the chunk counts and the
+// histogram, before any of them is known, places them in LDS at the chunk's
+// offset and histograms their low digits on the way; a chunk that kept more
+// reads the rest afterwards.  With more chunks the offsets come first, then
+// each candidate is fetched from its chunk's list.
+constexpr int kSpecPerChunk = 8 * 64;           // 8 candidates per lane
+
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
   __shared__ int offs[kMaxSelChunks + 1];
   __shared__ uint2 list[kListCap];
   __shared__ int scan_scratch[kSelNT / 64];
+  __shared__ int2 wave_tot[kSelNT / 64];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2;
 
   const int b = blockIdx.x;
@@ -218,31 +263,81 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     select_all(a, b, n, kSelNT);
     return;
   }
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   const uint32_t* counts = a.chunk_counts + (size_t)b * kMaxSelChunks;
   const uint2* cand_row = a.cand + (size_t)b * a.stride;
   const int n_chunks = (n + kFiltChunk - 1) / kFiltChunk;
+  const bool direct = n_chunks <= kSelWaves;
 
+  // direct plan: this lane's 8 candidates of chunk `wave` (entries of the
+  // row past its end read entry 0 and are never used) and the chunk counts
+  uint4 sv[4];
+  int my_count = 0;
+  if (direct) {
+    if (wave < n_chunks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = wave * kFiltChunk + 8 * lane + 2 * j;
+        sv[j] = *reinterpret_cast<const uint4*>(cand_row + (e < a.stride ? e : 0));
+      }
+    }
+    my_count = lane < n_chunks ? (int)counts[lane] : 0;
+  }
   const DigitBins<kSelNT> bins = load_digit_bins<kSelNT>(h1);
   for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
+  auto note = [&](int f, uint2 c) {       // candidate f of the concatenated lists
+    if (f < kListCap) list[f] = c;
+    if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
+  };
 
   int total = 0;
-  for (int c0 = 0; c0 < n_chunks; c0 += kSelNT) {
-    const int c = c0 + tid;
-    const int v = c < n_chunks ? (int)counts[c] : 0;
-    int round_total;
-    const int pre = block_exclusive_scan<kSelNT>(v, scan_scratch, &round_total);
-    if (c < n_chunks) offs[c] = total + pre;
-    total += round_total;
+  if (direct) {
+    int off = 0;
+#pragma unroll
+    for (int c = 0; c < kSelWaves; ++c) {
+      const int v = __builtin_amdgcn_readlane(my_count, c);
+      off += c < wave ? v : 0;
+      total += v;
+    }
+    if (lane == 0 && wave < n_chunks) offs[wave] = off;
+    if (tid == 0) offs[n_chunks] = total;
+    if (wave < n_chunks) {
+      const int cnt = __builtin_amdgcn_readlane(my_count, wave);
+      const uint2 e[8] = {make_uint2(sv[0].x, sv[0].y), make_uint2(sv[0].z, sv[0].w),
+                          make_uint2(sv[1].x, sv[1].y), make_uint2(sv[1].z, sv[1].w),
+                          make_uint2(sv[2].x, sv[2].y), make_uint2(sv[2].z, sv[2].w),
+                          make_uint2(sv[3].x, sv[3].y), make_uint2(sv[3].z, sv[3].w)};
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (8 * lane + k < cnt) note(off + 8 * lane + k, e[k]);
+      for (int i = kSpecPerChunk + lane; i < cnt; i += 64)
+        note(off + i, cand_row[(size_t)wave * kFiltChunk + i]);
+    }
+  } else {
+    for (int c0 = 0; c0 < n_chunks; c0 += kSelNT) {
+      const int c = c0 + tid;
+      const int v = c < n_chunks ? (int)counts[c] : 0;
+      int round_total;
+      const int pre = block_exclusive_scan<kSelNT>(v, scan_scratch, &round_total);
+      if (c < n_chunks) offs[c] = total + pre;
+      total += round_total;
+    }
+    if (tid == 0) offs[n_chunks] = total;
+    __syncthreads();
+    // each wave walks whole chunks, its lanes over consecutive candidates
+    for (int c = wave; c < n_chunks; c += kSelWaves) {
+      const int o = offs[c], cnt = offs[c + 1] - o;
+      for (int i = lane; i < cnt; i += 64) note(o + i, cand_row[(size_t)c * kFiltChunk + i]);
+    }
   }
-  if (tid == 0) offs[n_chunks] = total;
   __syncthreads();
 
   // entry f of the concatenated slot lists (already in entry order)
-  auto get_global = [&](int f) -> uint2 {
+  auto get = [&](int f) -> uint2 {
+    if (f < kListCap) return list[f];
     int lo = 0, hi = n_chunks - 1;          // largest c with offs[c] <= f
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -250,34 +345,12 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     }
     return cand_row[(size_t)lo * kFiltChunk + (f - offs[lo])];
   };
-  const bool cached = total <= kListCap;
-  if (cached) {             // every candidate into LDS, 6 loads in flight per thread
-    uint2 v[kListCap / kSelNT];
-#pragma unroll
-    for (int e = 0; e < kListCap / kSelNT; ++e) {
-      const int f = e * kSelNT + tid;
-      if (f < total) v[e] = get_global(f);
-    }
-#pragma unroll
-    for (int e = 0; e < kListCap / kSelNT; ++e) {
-      const int f = e * kSelNT + tid;
-      if (f < total) list[f] = v[e];
-    }
-    __syncthreads();
-  }
-  auto get = [&](int f) -> uint2 { return cached ? list[f] : get_global(f); };
-
-  for (int f = tid; f < total; f += kSelNT) {
-    const uint2 c = get(f);
-    if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
-  }
-  __syncthreads();
   find_digit<kSelNT>(hist2, K - sh_above1, scan_scratch, &sh_t2, &sh_above2);
   const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
   const int need_ties = K - sh_above1 - sh_above2;
   int32_t* out = a.out_idx + (size_t)b * K;
   const int written = emit_in_order<kSelNT>(
-      get, total, tau, need_ties, K, scan_scratch,
+      get, total, tau, need_ties, K, wave_tot,
       [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
   for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
   if (tid == 0) a.out_count[b] = written;

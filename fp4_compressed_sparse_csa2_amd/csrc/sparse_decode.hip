@@ -59,13 +59,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Dequantise 16 channels: 8 code bytes (two words) with E4M3 scale byte sc.
-// The hardware converter decodes E2M1 exactly at scale 1.0; the product with
-// the E4M3 scale (<= 5 significant bits in total) is exact in f16.
-__device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, uint32_t sc, half8& lo,
+// Dequantise 16 channels: 8 code bytes (two words) and their E4M3 scale s,
+// given as the f16 pair {s, s}.  The hardware converter decodes E2M1 exactly
+// at scale 1.0; the product with the E4M3 scale (<= 5 significant bits in
+// total) is exact in f16.
+__device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, half2v s2, half8& lo,
                                           half8& hi) {
-  const _Float16 s = (_Float16)e4m3_value(sc & 0x7Fu);
-  const half2v s2 = {s, s};
   uint4 u0, u1;
   u0.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2);
   u0.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2);
@@ -77,6 +76,13 @@ __device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, uint32_t sc,
   u1.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * s2);
   lo = __builtin_bit_cast(half8, u0);
   hi = __builtin_bit_cast(half8, u1);
+}
+
+// Four E4M3 scale bytes (sign cleared) as two f16 pairs, exactly, by the
+// hardware FP8 converter at scale 1.0.
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, half2v& s01, half2v& s23) {
+  s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w & 0x7F7F7F7Fu, 1.0f, false);
+  s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w & 0x7F7F7F7Fu, 1.0f, true);
 }
 
 __device__ __forceinline__ half8 bf16x8_to_f16(uint4 v) {
@@ -371,8 +377,10 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     l_q = l_q * alpha + sum_across_rows(psum);
     m_q = m_new;
     *reinterpret_cast<half4*>(Pt + lc * kPStride + wave * 16 + lg * 4) = ph;
+    if (__ballot(alpha != 1.0f)) {      // wave-uniform: skipped once the maxima settle
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+    }
     __syncthreads();
 
     // O^T[wave's D/4 dims][16 heads] += X^T P^T
@@ -413,17 +421,23 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 
   // ---- FP4 tiles
   auto fp4_tile = [&](const RowPart<D>& rp, long long rk) {
+    // the E4M3 scales of this lane's groups as f16; a token that is not
+    // real gets scale 0, so that its X row is exactly zero whatever the
+    // bytes it loaded (its weight in P is zero as well)
     const bool ok = rk >= 0;
+    half2v sc[4];
+    e4m3x4_to_f16(ok ? rp.s.x : 0u, sc[0], sc[1]);
+    if constexpr (D / 64 > 4) e4m3x4_to_f16(ok ? rp.s.y : 0u, sc[2], sc[3]);
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < DQ / 16; ++g) {
       const uint4 c4 = rp.c[g / 2];
       const uint32_t w0 = (g & 1) ? c4.z : c4.x, w1 = (g & 1) ? c4.w : c4.y;
-      const uint32_t sc = ((g < 4 ? rp.s.x : rp.s.y) >> (8 * (g & 3))) & 0xFFu;
+      const half2v sp = sc[g / 2];
+      const half2v s2 = (g & 1) ? __builtin_shufflevector(sp, sp, 1, 1)
+                                : __builtin_shufflevector(sp, sp, 0, 0);
       half8 lo, hi;
-      dequant16(w0, w1, sc, lo, hi);
-      lo = ok ? lo : half8{};
-      hi = ok ? hi : half8{};
+      dequant16(w0, w1, s2, lo, hi);
       *reinterpret_cast<half8*>(xrow + 16 * g) = lo;
       *reinterpret_cast<half8*>(xrow + 16 * g + 8) = hi;
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qf[2 * g], s0, 0, 0, 0);

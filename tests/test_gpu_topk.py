@@ -1,8 +1,9 @@
 """GPU parity of csa2_index_topk against the oracle: int32 scores and Top-K
 indices bit-exact (ties to the lower position), on small shapes and the edge
 cases of the selection (planted ties, all-equal scores, K = 0, K >= number of
-candidates, context shorter than the window, several bitmap segments, paged
-ragged batches).  Full-size workloads are in test_gpu_configs.py."""
+candidates, context shorter than the window, kept candidates past the
+one-block selection's on-chip list, the multi-block plan for long sequences,
+paged ragged batches).  Full-size workloads are in test_gpu_configs.py."""
 import numpy as np
 import pytest
 import torch
@@ -76,9 +77,24 @@ def test_ties_go_to_lower_positions(mode):
         _check(gc, q, K)
 
 
-def test_several_bitmap_segments_and_large_K():
+@pytest.mark.parametrize("mode", ["planted", "zeros"])
+def test_ties_past_the_lds_candidate_list(mode):
+    """~20K candidates per sequence: with all scores equal every candidate is
+    kept, more than the one-block selection holds on chip, so the rest go
+    through its global overflow area."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=20000)
+    log(f"topk ties L=20000 mode={mode}")
+    gc = GpuCache(wl, keys_fn=_tie_keys(mode))
+    q = gen.idx_query(wl)
+    for K in (2048, 7000, 19000):
+        _check(gc, q, K)
+
+
+def test_multi_block_plan_and_large_K():
+    """150K candidates: longer than the one-block selection takes, so the
+    filter + final plan runs; K = 65536 overflows its on-chip list too."""
     wl = gen.WORKLOADS["tiny"].with_(L=150_000, Di=64)
-    log("topk L=150000 (3 bitmap segments)")
+    log("topk L=150000 (multi-block plan)")
     gc = GpuCache(wl, keep_kv=False)
     q = gen.idx_query(wl)
     for K in (2048, 65536):
