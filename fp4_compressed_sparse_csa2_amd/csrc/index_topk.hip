@@ -52,33 +52,42 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
   const int chunk0 = blockIdx.x * kChunk;
   if (chunk0 >= n) return;
   const bool do_hist = K > 0 && n > K;
-  if (do_hist) {
-    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
-    __syncthreads();
-  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
+  __builtin_amdgcn_sched_barrier(0);     // the query goes out before the keys
   const int32_t* pt = page_table + (size_t)b * max_pages;
   int32_t* sc_row = scores + (size_t)b * row_stride(max_ctx);
   int32_t* user_row = out_scores ? out_scores + (size_t)b * max_ctx : nullptr;
   // after the lane-group sums, lane l keeps the score of page row ppos
   const int ppos = PPL * (lane % LPP) + lane / LPP;
 
-  const int lp0 = chunk0 / kPage + wave * kPagesPerWave;
+  // the wave's pages: a wave-uniform index, so the page-table reads are
+  // scalar loads that all go out before any key load waits on them
+  const int lp0 = chunk0 / kPage + __builtin_amdgcn_readfirstlane(wave) * kPagesPerWave;
+  int pg[kPagesPerWave];
+#pragma unroll
+  for (int pi = 0; pi < kPagesPerWave; ++pi) {
+    const int lp = lp0 + pi;
+    pg[pi] = (lp * kPage < n) ? pt[lp] : -1;
+  }
+  // then every key load, unconditionally (a page that is not live reads
+  // page 0, which always exists, and is skipped), so that page pi's compute
+  // waits only for its own loads
   uint4 v[kPagesPerWave][LPP];
   bool live[kPagesPerWave];
 #pragma unroll
-  for (int pi = 0; pi < kPagesPerWave; ++pi) {          // issue every load first
-    const int lp = lp0 + pi;
-    const int pg = (lp * kPage < n) ? pt[lp] : -1;
-    live[pi] = pg >= 0 && pg < num_pages;
-    if (live[pi]) {
-      const uint4* kp =
-          reinterpret_cast<const uint4*>(pages + (size_t)pg * page_bytes + keys_off);
+  for (int pi = 0; pi < kPagesPerWave; ++pi) {
+    live[pi] = pg[pi] >= 0 && pg[pi] < num_pages;
+    const uint4* kp = reinterpret_cast<const uint4*>(
+        pages + (size_t)(live[pi] ? pg[pi] : 0) * page_bytes + keys_off);
 #pragma unroll
-      for (int j = 0; j < LPP; ++j) v[pi][j] = kp[j * 64 + lane];
-    }
+    for (int j = 0; j < LPP; ++j) v[pi][j] = kp[j * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);   // keep the pages' loads in page order
+  }
+  if (do_hist) {                         // while the keys are on their way
+    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+    __syncthreads();
   }
 #pragma unroll
   for (int pi = 0; pi < kPagesPerWave; ++pi) {
@@ -99,14 +108,17 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
       if (user_row) user_row[p] = keep;
       if (do_hist) atomicAdd(&hist[score_key(keep) >> 11], 1u);
     }
+    __builtin_amdgcn_sched_barrier(0);   // pages in arrival order
   }
   if (do_hist) {
     __syncthreads();
     uint32_t* g = ctrl + (size_t)b * kCtrlWords + kCtrlHist1;
-    for (int i = threadIdx.x; i < kBins; i += kBlock) {
-      const uint32_t h = hist[i];
-      if (h) atomicAdd(&g[i], h);
-    }
+    uint32_t h[kBins / kBlock];
+#pragma unroll
+    for (int k = 0; k < kBins / kBlock; ++k) h[k] = hist[k * kBlock + threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kBins / kBlock; ++k)
+      if (h[k]) atomicAdd(&g[k * kBlock + threadIdx.x], h[k]);
   }
 }
 

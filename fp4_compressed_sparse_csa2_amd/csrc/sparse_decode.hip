@@ -184,30 +184,27 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   const int b = grp / n_splits, split = grp % n_splits;
   const int unit = b * n_hg + hg;
 
-  int L = ctx_len[b];
-  L = L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
-  const int n_glob = L > kWindow ? L - kWindow : 0;     // selectable positions
-  int cnt = idx_count[b];
-  cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
-  const int n_win = L < kWindow ? L : kWindow;
-  // The sequence's tiles: two of window rows, then ceil(K/64) of selected
-  // FP4 rows.  With one split a block takes them all; with several, splits 0
-  // and 1 take one window tile each and split s >= 2 takes FP4 tiles
-  // [(s-2)*split_tiles, (s-1)*split_tiles).
-  const int tw = (n_win + kTile - 1) / kTile;            // window tiles holding tokens
-  const int tf = (cnt + kTile - 1) / kTile;              // FP4 tiles holding tokens
-  int wa = 0, wb = 0, fa = 0, fb = 0;                    // this block's tiles
+  // per-sequence scalars, used only after every prologue load is issued
+  const int L_raw = ctx_len[b];
+  const int cnt_raw = idx_count[b];
+  // This block's tiles as fixed by the plan alone: window tiles [wa, wb0)
+  // and FP4 tiles [fa, fb0) of the ceil(K/64) a sequence can have.  With one
+  // split a block takes them all; with several, splits 0 and 1 take one
+  // window tile each and split s >= 2 takes FP4 tiles
+  // [(s-2)*split_tiles, (s-1)*split_tiles).  The sequence's length and Top-K
+  // count trim them later.
+  const int tiles_k = (K + kTile - 1) / kTile;
+  int wa = 0, wb0 = 0, fa = 0, fb0 = 0;
   if (n_splits == 1) {
-    wb = tw;
-    fb = tf;
+    wb0 = kWinTiles;
+    fb0 = tiles_k;
   } else if (split < kWinTiles) {
     wa = split;
-    wb = min(split + 1, tw);
+    wb0 = split + 1;
   } else {
     fa = (split - kWinTiles) * split_tiles;
-    fb = min(fa + split_tiles, tf);
+    fb0 = min(fa + split_tiles, tiles_k);
   }
-  const int nf = fb > fa ? fb - fa : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
@@ -219,38 +216,33 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   const int32_t* idx_row = idx + (size_t)b * K;
   const uint16_t* swa_b = swa + (size_t)b * kWindow * D;
 
-  // ---- prologue: every load that depends on nothing is issued here
-  // window rows of the first window tile (token k of the window is position L - n_win + k)
+  // ---- prologue: every load is issued before any result is used
+  // window rows by ring slot: window tile t holds slots 64t .. 64t+63 (the
+  // softmax does not depend on the order of the window's tokens); slot s
+  // holds a token of the window iff s < min(L, 128)
   uint4 wreg[DQ / 8];
   auto load_win = [&](int t) {
-    const int k = t * kTile + tok;
-    const int p = L - n_win + (k < n_win ? k : 0);
     const uint4* src =
-        reinterpret_cast<const uint4*>(swa_b + (size_t)(p % kWindow) * D + lg * DQ);
+        reinterpret_cast<const uint4*>(swa_b + (size_t)(t * kTile + tok) * D + lg * DQ);
 #pragma unroll
     for (int i = 0; i < DQ / 8; ++i) wreg[i] = src[i];
   };
-  if (wa < wb) load_win(wa);
-  // positions of the first FP4 tiles.  A position is carried as the raw
-  // loaded index (an unconditional load of a clamped address) plus a flag
-  // computed without it, so that no load result is consumed in the stage
-  // that issues it.
+  if (wa < wb0) load_win(wa);
+  // positions of the first FP4 tiles: unconditional loads of clamped entries
+  // of the index row; which of them are real is decided from the count
   auto pos_load = [&](int f) -> int {
     const int j = f * kTile + tok;
-    return idx_row[j < cnt ? j : cnt - 1];
+    return idx_row[j < K ? j : K - 1];
   };
-  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + tok < cnt; };
   int p0 = -1, p1 = -1, p2 = -1, p3 = -1;
-  bool ok3 = false;
-  if (fa < fb) {
+  if (fa < fb0) {
     p0 = pos_load(fa);
     p1 = pos_load(fa + 1);
     p2 = pos_load(fa + 2);
     p3 = pos_load(fa + 3);
-    ok3 = pos_ok(fa + 3);
   }
   int ptv[PTC ? kPtCache / kBlock : 1];
-  if (PTC && fa < fb) {
+  if (PTC && fa < fb0) {
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i) {
       const int e = i * kBlock + tid;
@@ -296,7 +288,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
       *reinterpret_cast<half8*>(dst + 8 * i) = h;
     }
   }
-  if (PTC && fa < fb) {
+  if (PTC && fa < fb0) {
 #pragma unroll
     for (int i = 0; i < kPtCache / kBlock; ++i)
       if (i * kBlock < max_pages) pt_lds[i * kBlock + tid] = ptv[i];
@@ -314,6 +306,16 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   // logits in log2 units: scale2 * (q~ . x) for head lc
   const float scale2 = ldexpf(scale, -q_exp[lc]) * kLog2e;
   __syncthreads();                      // the staging area becomes the X tile
+
+  const int L = L_raw < 0 ? 0 : (L_raw > max_pages * kPage ? max_pages * kPage : L_raw);
+  const int n_glob = L > kWindow ? L - kWindow : 0;     // selectable positions
+  const int cnt = cnt_raw < 0 ? 0 : (cnt_raw > K ? K : cnt_raw);
+  const int n_win = L < kWindow ? L : kWindow;
+  const int wb = min(wb0, (n_win + kTile - 1) / kTile);  // tiles that hold tokens
+  const int fb = min(fb0, (cnt + kTile - 1) / kTile);
+  const int nf = fb > fa ? fb - fa : 0;
+  auto pos_ok = [&](int f) -> bool { return f < fb && f * kTile + tok < cnt; };
+  bool ok3 = pos_ok(fa + 3);
 
   // page of a selected position (-1 if it is not a selectable position)
   auto page_of = [&](int p) -> int {
