@@ -195,6 +195,10 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ filter
+// Block = 4096 entries of one sequence.  Keeps the entries whose top digit is
+// at least t1 in entry order in the chunk's own slot list, counts them, and
+// adds the low digits of those whose top digit equals t1 to the sequence's
+// low-digit histogram.
 __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
   __shared__ int scan_scratch[kBlock / 64];
   __shared__ int sh_t1, sh_above1;
@@ -204,6 +208,7 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
   const int chunk = blockIdx.x, chunk0 = chunk * kFiltChunk;
   if (a.K == 0 || n <= a.K || chunk0 >= n) return;
   const int32_t* row = a.scores + (size_t)b * a.stride;
+  uint32_t* ctrl = a.hist1 + (size_t)b * kCtrlWords;
 
   // this thread's 16 scores and the block's share of the histogram, loaded together
   const int p0 = chunk0 + (int)threadIdx.x * kFiltPer;
@@ -213,48 +218,55 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 #pragma unroll
     for (int i = 0; i < kFiltPer / 4; ++i) sv[i] = src[i];
   }
-  const DigitBins<kBlock> bins = load_digit_bins<kBlock>(a.hist1 + (size_t)b * kCtrlWords);
+  const DigitBins<kBlock> bins = load_digit_bins<kBlock>(ctrl);
   find_digit_in<kBlock>(bins, a.K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
 
   uint32_t key[kFiltPer];
-  int nk = 0;
+  uint32_t keep = 0;                     // bit e: entry p0 + e is kept
 #pragma unroll
   for (int i = 0; i < kFiltPer / 4; ++i) {
     const int w[4] = {(int)sv[i].x, (int)sv[i].y, (int)sv[i].z, (int)sv[i].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t kk = score_key(w[k]);
-      const bool keep = p0 + 4 * i + k < n && (kk >> 11) >= t1;
-      key[4 * i + k] = keep ? kk : 0u;
-      nk += keep ? 1 : 0;
+      key[4 * i + k] = kk;
+      keep |= (p0 + 4 * i + k < n && (kk >> 11) >= t1) ? 1u << (4 * i + k) : 0u;
     }
   }
   int chunk_total;
-  int slot = block_exclusive_scan<kBlock>(nk, scan_scratch, &chunk_total);
+  int slot = block_exclusive_scan<kBlock>(__builtin_popcount(keep), scan_scratch, &chunk_total);
   uint2* dst = a.cand + (size_t)b * a.stride + chunk0;
 #pragma unroll
-  for (int e = 0; e < kFiltPer; ++e)
-    if (key[e] != 0u) dst[slot++] = make_uint2(key[e], (uint32_t)(p0 + e));
+  for (int e = 0; e < kFiltPer; ++e) {
+    if ((keep >> e) & 1u) {
+      dst[slot++] = make_uint2(key[e], (uint32_t)(p0 + e));
+      if ((key[e] >> 11) == t1) atomicAdd(&ctrl[kCtrlHist2 + (key[e] & (kBins - 1))], 1u);
+    }
+  }
   if (threadIdx.x == 0) a.chunk_counts[(size_t)b * kMaxSelChunks + chunk] = (uint32_t)chunk_total;
 }
 
 // ------------------------------------------------------------------ final
-// Direct plan (at most one chunk per wave): wave w requests the first
-// kSpecPerChunk candidates of chunk w together with the chunk counts and the
-// histogram, before any of them is known, places them in LDS at the chunk's
-// offset and histograms their low digits on the way; a chunk that kept more
-// reads the rest afterwards.  With more chunks the offsets come first, then
-// each candidate is fetched from its chunk's list.
+// One block per sequence.  Both digits of the threshold come from the two
+// histograms (one block scan), so every candidate is classified once: above
+// the threshold key tau, equal to it (the first need_ties of those, in entry
+// order, are selected) or below.
+// Direct plan (at most 16 chunks, none with more than kSpecPerChunk kept):
+// wave w requests the first kSpecPerChunk slots of chunk w together with the
+// counts and histograms, before any of them is known, and places its chunk's
+// picks from registers after one barrier.  Otherwise the slot lists are
+// concatenated in LDS (the overflow read from the lists themselves) and
+// emitted in order.
 constexpr int kSpecPerChunk = 8 * 64;           // 8 candidates per lane
 
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
-  __shared__ uint32_t hist2[kBins];
   __shared__ int offs[kMaxSelChunks + 1];
   __shared__ uint2 list[kListCap];
-  __shared__ int scan_scratch[kSelNT / 64];
-  __shared__ int2 wave_tot[kSelNT / 64];
-  __shared__ int sh_t1, sh_above1, sh_t2, sh_above2;
+  __shared__ unsigned long long scan64[kSelWaves];
+  __shared__ int scan_scratch[kSelWaves];
+  __shared__ int2 wave_tot[kSelWaves];
+  __shared__ int sh[4];
 
   const int b = blockIdx.x;
   const int n = sel_entries(a, b);
@@ -265,16 +277,18 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
+  uint32_t* h2 = h1 + kCtrlHist2;
   const uint32_t* counts = a.chunk_counts + (size_t)b * kMaxSelChunks;
   const uint2* cand_row = a.cand + (size_t)b * a.stride;
+  int32_t* out = a.out_idx + (size_t)b * K;
   const int n_chunks = (n + kFiltChunk - 1) / kFiltChunk;
-  const bool direct = n_chunks <= kSelWaves;
+  const bool few = n_chunks <= kSelWaves;
 
-  // direct plan: this lane's 8 candidates of chunk `wave` (entries of the
-  // row past its end read entry 0 and are never used) and the chunk counts
+  // this lane's 8 slots of chunk `wave` (slots past the row's end read entry
+  // 0 and are never used), the chunk counts and both histograms, together
   uint4 sv[4];
   int my_count = 0;
-  if (direct) {
+  if (few) {
     if (wave < n_chunks) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -284,39 +298,74 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     }
     my_count = lane < n_chunks ? (int)counts[lane] : 0;
   }
-  const DigitBins<kSelNT> bins = load_digit_bins<kSelNT>(h1);
-  for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
-  find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
-  const uint32_t t1 = (uint32_t)sh_t1;
-  auto note = [&](int f, uint2 c) {       // candidate f of the concatenated lists
-    if (f < kListCap) list[f] = c;
-    if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
-  };
+  const DigitBins<kSelNT> bins1 = load_digit_bins<kSelNT>(h1);
+  const DigitBins<kSelNT> bins2 = load_digit_bins<kSelNT>(h2);
+  find_two_digits<kSelNT>(bins1, bins2, K, scan64, sh);
+  const uint32_t tau = ((uint32_t)sh[0] << 11) | (uint32_t)sh[2];
+  const int need_ties = K - sh[1] - sh[3];
 
-  int total = 0;
-  if (direct) {
-    int off = 0;
+  int cmax = 0, off = 0;
+  if (few) {
 #pragma unroll
     for (int c = 0; c < kSelWaves; ++c) {
       const int v = __builtin_amdgcn_readlane(my_count, c);
+      cmax = v > cmax ? v : cmax;
       off += c < wave ? v : 0;
-      total += v;
     }
-    if (lane == 0 && wave < n_chunks) offs[wave] = off;
-    if (tid == 0) offs[n_chunks] = total;
-    if (wave < n_chunks) {
-      const int cnt = __builtin_amdgcn_readlane(my_count, wave);
-      const uint2 e[8] = {make_uint2(sv[0].x, sv[0].y), make_uint2(sv[0].z, sv[0].w),
-                          make_uint2(sv[1].x, sv[1].y), make_uint2(sv[1].z, sv[1].w),
-                          make_uint2(sv[2].x, sv[2].y), make_uint2(sv[2].z, sv[2].w),
-                          make_uint2(sv[3].x, sv[3].y), make_uint2(sv[3].z, sv[3].w)};
+  }
+  int written;
+  if (few && cmax <= kSpecPerChunk) {
+    // ---- direct: wave w holds chunk w's candidates 8*lane .. 8*lane+7
+    const int cnt = wave < n_chunks ? __builtin_amdgcn_readlane(my_count, wave) : 0;
+    const uint2 e[8] = {make_uint2(sv[0].x, sv[0].y), make_uint2(sv[0].z, sv[0].w),
+                        make_uint2(sv[1].x, sv[1].y), make_uint2(sv[1].z, sv[1].w),
+                        make_uint2(sv[2].x, sv[2].y), make_uint2(sv[2].z, sv[2].w),
+                        make_uint2(sv[3].x, sv[3].y), make_uint2(sv[3].z, sv[3].w)};
+    uint32_t gtm = 0, tiem = 0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (8 * lane + k < cnt) note(off + 8 * lane + k, e[k]);
-      for (int i = kSpecPerChunk + lane; i < cnt; i += 64)
-        note(off + i, cand_row[(size_t)wave * kFiltChunk + i]);
+    for (int k = 0; k < 8; ++k) {
+      const bool live = 8 * lane + k < cnt;
+      gtm |= (live && e[k].x > tau) ? 1u << k : 0u;
+      tiem |= (live && e[k].x == tau) ? 1u << k : 0u;
     }
+    // in-wave prefix counts of this lane's picks (at most 8 each: 4 ballots)
+    const uint32_t ng = __builtin_popcount(gtm), nt = __builtin_popcount(tiem);
+    int gpre = 0, tpre = 0, gw = 0, tw = 0;
+#pragma unroll
+    for (int bit = 0; bit < 4; ++bit) {
+      const uint64_t bg = __ballot((ng >> bit) & 1u), bt = __ballot((nt >> bit) & 1u);
+      gpre += lanes_below(bg) << bit;
+      tpre += lanes_below(bt) << bit;
+      gw += (int)__popcll(bg) << bit;
+      tw += (int)__popcll(bt) << bit;
+    }
+    if (lane == 0) wave_tot[wave] = make_int2(gw, tw);
+    __syncthreads();
+    int g = gpre, t = tpre, G = 0, T = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int2 v = wave_tot[w];
+      g += w < wave ? v.x : 0;
+      t += w < wave ? v.y : 0;
+      G += v.x;
+      T += v.y;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if ((gtm >> k) & 1u) {
+        const int slot = g + (t < need_ties ? t : need_ties);
+        if (slot < K) out[slot] = sel_id(a, b, e[k].y);
+        ++g;
+      } else if ((tiem >> k) & 1u) {
+        if (t < need_ties && g + t < K) out[g + t] = sel_id(a, b, e[k].y);
+        ++t;
+      }
+    }
+    const int nsel = G + (T < need_ties ? T : need_ties);
+    written = nsel < K ? nsel : K;
   } else {
+    // ---- general: concatenate the slot lists (offsets first)
+    int total = 0;
     for (int c0 = 0; c0 < n_chunks; c0 += kSelNT) {
       const int c = c0 + tid;
       const int v = c < n_chunks ? (int)counts[c] : 0;
@@ -330,31 +379,26 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     // each wave walks whole chunks, its lanes over consecutive candidates
     for (int c = wave; c < n_chunks; c += kSelWaves) {
       const int o = offs[c], cnt = offs[c + 1] - o;
-      for (int i = lane; i < cnt; i += 64) note(o + i, cand_row[(size_t)c * kFiltChunk + i]);
+      for (int i = lane; i < cnt && o + i < kListCap; i += 64)
+        list[o + i] = cand_row[(size_t)c * kFiltChunk + i];
     }
+    __syncthreads();
+    // entry f of the concatenated slot lists (already in entry order)
+    auto get = [&](int f) -> uint2 {
+      if (f < kListCap) return list[f];
+      int lo = 0, hi = n_chunks - 1;        // largest c with offs[c] <= f
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= f) lo = mid; else hi = mid - 1;
+      }
+      return cand_row[(size_t)lo * kFiltChunk + (f - offs[lo])];
+    };
+    written = emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot,
+                                    [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
   }
-  __syncthreads();
-
-  // entry f of the concatenated slot lists (already in entry order)
-  auto get = [&](int f) -> uint2 {
-    if (f < kListCap) return list[f];
-    int lo = 0, hi = n_chunks - 1;          // largest c with offs[c] <= f
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offs[mid] <= f) lo = mid; else hi = mid - 1;
-    }
-    return cand_row[(size_t)lo * kFiltChunk + (f - offs[lo])];
-  };
-  find_digit<kSelNT>(hist2, K - sh_above1, scan_scratch, &sh_t2, &sh_above2);
-  const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
-  const int need_ties = K - sh_above1 - sh_above2;
-  int32_t* out = a.out_idx + (size_t)b * K;
-  const int written = emit_in_order<kSelNT>(
-      get, total, tau, need_ties, K, wave_tot,
-      [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
   for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
   if (tid == 0) a.out_count[b] = written;
-  for (int i = tid; i < kBins; i += kSelNT) h1[i] = 0u;     // ready for the next call
+  for (int i = tid; i < 2 * kBins; i += kSelNT) h1[i] = 0u;   // both histograms, for the next call
 }
 
 // ------------------------------------------------------------------ host
