@@ -467,7 +467,7 @@ def main() -> int:
         "step_us_events": step_s * 1e6,
         "calls_us": calls,
         "calls_gbs": {"index_topk": topk_gbs, "sparse_decode": dec_gbs},
-        "roofline": {"kernel": "csa2_index_topk (index_score_kernel + select_single_kernel)",
+        "roofline": {"kernel": "csa2_index_topk (" + ", ".join(STEP_KERNELS["index_topk"]) + ")",
                      "bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": topk_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": calls["index_topk"], "bytes_per_launch": nbytes["index_topk"]},
