@@ -57,6 +57,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, vendor figure
 WORKLOAD = "b8_64k"
 
 
@@ -205,6 +206,97 @@ def capture(S: Setup, fn, rs):
     return g
 
 
+def time_call(S: Setup, fn, R: int, reps: int = 20) -> float:
+    """Microseconds per call of fn(r): a graph of 4 rounds over the R replicas,
+    replayed reps times between HIP events on the stream it runs on."""
+    torch = S.torch
+    g = capture(S, fn, [r for _ in range(4) for r in range(R)])
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * 4 * R)
+
+
+def copy_gbs(torch, nbytes: int = 1 << 30) -> float:
+    """Device-to-device copy rate (read + write bytes per second) of a plain
+    torch copy: the stream reference the roofline fraction can be read against."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 5
+    del a, b
+    return 2 * nbytes / t / 1e9
+
+
+def chain_calls(S: Setup) -> dict:
+    """The Reindex / Reuse rows timed on this cache, with the shapes of the
+    three-layer chain workload: a Full Top-K pool of 8192, a Reindex layer
+    refiltering it to 2048 with its own indexer query, and the decodes of the
+    Reindex layer and of a Reuse layer (own queries, same indices)."""
+    torch, csa2, gen = S.torch, S.csa2, S.gen
+    wl, dev, R = S.wl, S.dev, len(S.caches)
+    wlc = gen.WORKLOADS["chain_64k"]
+    B, Kf, K2 = wl.B, wlc.K, wlc.K2
+    pool = torch.empty((B, Kf), dtype=torch.int32, device=dev)
+    pc = torch.empty((B,), dtype=torch.int32, device=dev)
+    idx2 = torch.empty((B, K2), dtype=torch.int32, device=dev)
+    c2 = torch.empty((B,), dtype=torch.int32, device=dev)
+    q1 = S.t(gen.idx_query(wlc, 1))
+    qa, qb = S.t(gen.query(wlc, 1)), S.t(gen.query(wlc, 2))
+    outs = [torch.empty((B, wl.H, wl.D), dtype=torch.float32, device=dev) for _ in range(2)]
+    lses = [torch.empty((B, wl.H), dtype=torch.float32, device=dev) for _ in range(2)]
+    ws = [csa2.Workspace(dev) for _ in range(4)]
+    sigma = float(gen.softmax_scale(wlc))
+
+    def full(r):
+        csa2.index_topk(S.caches[r], S.ctx, S.max_ctx, S.q_idx, Kf, ws[0], out_idx=pool,
+                        out_count=pc)
+
+    def reindex(r):
+        csa2.reindex(S.caches[r], q1, pool, pc, K2, ws[1], out_idx=idx2, out_count=c2)
+
+    def dec_reindex_layer(r):
+        csa2.sparse_decode(S.caches[r], S.ctx, qa, sigma, idx2, c2, S.rings[r], ws[2],
+                           out=outs[0], lse=lses[0])
+
+    def dec_reuse_layer(r):
+        csa2.sparse_decode(S.caches[r], S.ctx, qb, sigma, idx2, c2, S.rings[r], ws[3],
+                           out=outs[1], lse=lses[1])
+
+    for r in range(R):                       # eager pass sizes the workspaces
+        full(r)
+        reindex(r)
+        dec_reindex_layer(r)
+        dec_reuse_layer(r)
+    torch.cuda.synchronize()
+    t = {name: time_call(S, fn, R) for name, fn in (
+        ("full_index_topk_8192", full), ("reindex_8192_to_2048", reindex),
+        ("sparse_decode_reindex_layer", dec_reindex_layer),
+        ("sparse_decode_reuse_layer", dec_reuse_layer))}
+    rbytes = B * (Kf * (4 + wl.Di) + wl.Di + 4 * K2)
+    return {"workload": "chain_64k shapes on the b8_64k cache: Full Top-K 8192 -> Reindex "
+                        "Top-K 2048 -> decode of the Reindex layer and of a Reuse layer",
+            "calls_us": t,
+            "reindex_layer_step_us": t["reindex_8192_to_2048"] + t["sparse_decode_reindex_layer"],
+            "reuse_layer_step_us": t["sparse_decode_reuse_layer"],
+            "reindex_algorithmic_bytes": rbytes,
+            "reindex_gbs": rbytes / (t["reindex_8192_to_2048"] * 1e-6) / 1e9}
+
+
 def parity_check(S: Setup) -> str:
     """Sequences 0 and B-1 of the eager result against the oracle: indices
     bit-exact, outputs and LSE within 2e-3."""
@@ -268,24 +360,26 @@ def gpu_bench(args, S: Setup):
     ev_ms = e0.elapsed_time(e1)
 
     # per-call durations: graphs of one call kind over the replicas
-    calls = {}
-    reps = 20
-    for name, fn in (("append", S.append), ("index_topk", S.index_topk),
-                     ("sparse_decode", S.decode)):
-        g = capture(S, fn, [r for _ in range(4) for r in range(R)])
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        calls[name] = a.elapsed_time(b) * 1e3 / (reps * 4 * R)      # us per call
+    calls = {name: time_call(S, fn, R) for name, fn in (
+        ("append", S.append), ("index_topk", S.index_topk), ("sparse_decode", S.decode))}
     torch.cuda.synchronize()
     for t, r in zip((S.idx, S.cnt, S.out, S.lse), ref):
         assert torch.equal(t, r), "per-call replay differs from the eager step"
-    return wall, ev_ms, calls, parity
+
+    # spread of the step time over replays of the big graph, and a warm step
+    # (one replica, its keys resident in the last-level cache)
+    per_step = []
+    for _ in range(10):
+        e0.record(stream)
+        big.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_step.append(e0.elapsed_time(e1) * 1e3 / S_big)
+    warm_us = time_call(S, S.step, 1)
+    spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+              "p90": float(np.percentile(per_step, 90)), "warm_one_replica": warm_us,
+              "replays": len(per_step), "steps_per_replay": S_big}
+    return wall, ev_ms, calls, parity, spread
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -432,7 +526,9 @@ def main() -> int:
         return counter_run(args)
     S = Setup(args.replicas)
     wl = S.wl
-    wall, ev_ms, calls, parity = gpu_bench(args, S)
+    wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
+    chain = chain_calls(S)
+    copy_rate = copy_gbs(torch)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
     step_bytes = sum(nbytes.values())
@@ -441,6 +537,8 @@ def main() -> int:
     topk_s = calls["index_topk"] * 1e-6
     topk_gbs = nbytes["index_topk"] / topk_s / 1e9
     dec_gbs = nbytes["sparse_decode"] / (calls["sparse_decode"] * 1e-6) / 1e9
+    dec_flops = 4 * H * D * (K + 128) * B                 # QK^T and PV over selected + window
+    dec_tflops = dec_flops / (calls["sparse_decode"] * 1e-6) / 1e12
     traffic = measured_traffic("index_topk")
     res = {
         "metric": "decode attention queries/sec and achieved HBM GB/s (% of peak) at 64K ctx",
@@ -467,9 +565,16 @@ def main() -> int:
         "step_us_events": step_s * 1e6,
         "calls_us": calls,
         "calls_gbs": {"index_topk": topk_gbs, "sparse_decode": dec_gbs},
+        "step_us_spread": spread,
+        "sparse_decode_mfma": {"flops_per_call": dec_flops, "tflops": dec_tflops,
+                               "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                               "frac": dec_tflops / MFMA_F16_PEAK_TFLOPS},
+        "copy_reference_gbs": copy_rate,
+        "chain": chain,
         "roofline": {"kernel": "csa2_index_topk (" + ", ".join(STEP_KERNELS["index_topk"]) + ")",
                      "bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": topk_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac_of_copy_reference": topk_gbs / copy_rate,
                      "launch_us": calls["index_topk"], "bytes_per_launch": nbytes["index_topk"]},
         "parity": parity,
     }

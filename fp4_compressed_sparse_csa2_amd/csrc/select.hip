@@ -252,15 +252,17 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 // histograms (one block scan), so every candidate is classified once: above
 // the threshold key tau, equal to it (the first need_ties of those, in entry
 // order, are selected) or below.
-// Direct plan (at most 16 chunks, none with more than kSpecPerChunk kept):
-// wave w requests the first kSpecPerChunk slots of chunk w together with the
-// counts and histograms, before any of them is known, and places its chunk's
-// picks from registers after one barrier.  Otherwise the slot lists are
-// concatenated in LDS (the overflow read from the lists themselves) and
+// Direct plan (at most 16 chunks, none with more kept than its wave holds):
+// wave w requests the first 64*SPL slots of chunk w (SPL = 8 or 16 per lane,
+// chosen by the host from the expected share of K per chunk) together with
+// the counts and histograms, before any of them is known, and places its
+// chunk's picks from registers after one barrier.  Otherwise the slot lists
+// are concatenated in LDS (the overflow read from the lists themselves) and
 // emitted in order.
-constexpr int kSpecPerChunk = 8 * 64;           // 8 candidates per lane
+template <int SPL>
 
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
+  constexpr int spl = SPL;
   __shared__ int offs[kMaxSelChunks + 1];
   __shared__ uint2 list[kListCap];
   __shared__ unsigned long long scan64[kSelWaves];
@@ -284,15 +286,16 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   const int n_chunks = (n + kFiltChunk - 1) / kFiltChunk;
   const bool few = n_chunks <= kSelWaves;
 
-  // this lane's 8 slots of chunk `wave` (slots past the row's end read entry
-  // 0 and are never used), the chunk counts and both histograms, together
-  uint4 sv[4];
+  // this lane's spl slots of chunk `wave` (slots past the row's end read
+  // entry 0 and are never used), the chunk counts and both histograms,
+  // together
+  uint4 sv[spl / 2];
   int my_count = 0;
   if (few) {
     if (wave < n_chunks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = wave * kFiltChunk + 8 * lane + 2 * j;
+      for (int j = 0; j < spl / 2; ++j) {
+        const int e = wave * kFiltChunk + spl * lane + 2 * j;
         sv[j] = *reinterpret_cast<const uint4*>(cand_row + (e < a.stride ? e : 0));
       }
     }
@@ -314,25 +317,27 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     }
   }
   int written;
-  if (few && cmax <= kSpecPerChunk) {
-    // ---- direct: wave w holds chunk w's candidates 8*lane .. 8*lane+7
+  if (few && cmax <= 64 * spl) {
+    // ---- direct: wave w holds chunk w's candidates spl*lane .. spl*lane+spl-1
     const int cnt = wave < n_chunks ? __builtin_amdgcn_readlane(my_count, wave) : 0;
-    const uint2 e[8] = {make_uint2(sv[0].x, sv[0].y), make_uint2(sv[0].z, sv[0].w),
-                        make_uint2(sv[1].x, sv[1].y), make_uint2(sv[1].z, sv[1].w),
-                        make_uint2(sv[2].x, sv[2].y), make_uint2(sv[2].z, sv[2].w),
-                        make_uint2(sv[3].x, sv[3].y), make_uint2(sv[3].z, sv[3].w)};
+    uint2 e[spl];
+#pragma unroll
+    for (int j = 0; j < spl / 2; ++j) {
+      e[2 * j] = make_uint2(sv[j].x, sv[j].y);
+      e[2 * j + 1] = make_uint2(sv[j].z, sv[j].w);
+    }
     uint32_t gtm = 0, tiem = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool live = 8 * lane + k < cnt;
+    for (int k = 0; k < spl; ++k) {
+      const bool live = spl * lane + k < cnt;
       gtm |= (live && e[k].x > tau) ? 1u << k : 0u;
       tiem |= (live && e[k].x == tau) ? 1u << k : 0u;
     }
-    // in-wave prefix counts of this lane's picks (at most 8 each: 4 ballots)
+    // in-wave prefix counts of this lane's picks (at most spl each)
     const uint32_t ng = __builtin_popcount(gtm), nt = __builtin_popcount(tiem);
     int gpre = 0, tpre = 0, gw = 0, tw = 0;
 #pragma unroll
-    for (int bit = 0; bit < 4; ++bit) {
+    for (int bit = 0; (1 << bit) <= spl; ++bit) {
       const uint64_t bg = __ballot((ng >> bit) & 1u), bt = __ballot((nt >> bit) & 1u);
       gpre += lanes_below(bg) << bit;
       tpre += lanes_below(bt) << bit;
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       T += v.y;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < spl; ++k) {
       if ((gtm >> k) & 1u) {
         const int slot = g + (t < need_ties ? t : need_ties);
         if (slot < K) out[slot] = sel_id(a, b, e[k].y);
@@ -411,7 +416,13 @@ hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st) {
   hipLaunchKernelGGL(select_filter_kernel, dim3(chunks, a.batch), dim3(kBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_final_kernel, dim3(a.batch), dim3(kSelNT), 0, st, a);
+  // 16 candidates per lane in the direct plan when a chunk is expected to
+  // keep more than ~400 (K's share of a chunk, with 25% to spare)
+  const bool wide = (long long)a.K * kFiltChunk * 5 > (long long)max_entries * 4 * 8 * 64;
+  if (wide)
+    hipLaunchKernelGGL(select_final_kernel<16>, dim3(a.batch), dim3(kSelNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_final_kernel<8>, dim3(a.batch), dim3(kSelNT), 0, st, a);
   return hipGetLastError();
 }
 
