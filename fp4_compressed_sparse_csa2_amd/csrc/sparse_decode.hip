@@ -13,20 +13,24 @@
 // (sequence, group of 16 heads) and a run of consecutive tiles (a split);
 // 4 waves.  All splits of one (sequence, head group) land on one XCD.
 //
-// The block starts by loading, all at once, its queries, its first window
-// rows, the positions of its first four FP4 tiles and (when it fits in LDS)
-// the sequence's page table.  The FP4 tiles then run as a pipeline: while
-// tile f computes, the rows of f+1, the page of f+3 and the position of f+4
-// are in flight.  Per tile:
-//   1. dequantise the tile into LDS as f16 [64][D+8] (FP4 -> exact E2M1 with
-//      the hardware converter at scale 1.0, then an exact f16 multiply by the
-//      E4M3 scale; window rows bf16 -> f16, exact);
-//   2. wave w computes S^T = X[16w..16w+16) Q^T with MFMA 16x16x32 f16
-//      (queries pre-scaled per head by a power of two so that their f16 copy
-//      is exact), tile max per head through LDS;
+// The block starts by issuing every load that depends on nothing: its
+// queries, its first window rows, the positions of its first four FP4 tiles
+// and (when it fits in LDS) the sequence's page table.  The queries are
+// converted once per block to exact f16 copies of q * 2^e (e per head) and
+// staged in LDS.  The FP4 rows of a short run are all requested at once; a
+// long run is a pipeline (while tile f computes, the rows of f+1, the page
+// of f+3 and the position of f+4 are in flight).  Per tile, with gather lane
+// (c, g) of wave w holding token 16w + c and channels [gD/4, (g+1)D/4):
+//   1. dequantise its channels (FP4 -> exact E2M1 with the hardware
+//      converter at scale 1.0, then an exact f16 multiply by the E4M3 scale;
+//      window rows bf16 -> f16, exact) and write them to the LDS tile;
+//   2. S^T for the wave's 16 tokens and the 16 heads on MFMA 16x16x32 f16
+//      straight from those registers (the contraction visits the channels in
+//      the order the lanes hold them, the same for the queries); tile max per
+//      head through LDS;
 //   3. online softmax in the exp2 domain, P (f16) to LDS;
 //   4. wave w accumulates O[16 heads][D/4 slice] += P X with MFMA, the X
-//      operand read token-major by ds_read_b64_tr_b16.
+//      operand read token-major from the LDS tile by ds_read_b64_tr_b16.
 // A split writes (m, l, unnormalised O); a combine kernel merges the splits
 // of each (sequence, head) by their LSE, every load of a thread in flight at
 // once.
