@@ -57,7 +57,10 @@ __device__ inline void find_digit_in(const DigitBins<NT>& d, int need, int* scan
   int s = 0;
 #pragma unroll
   for (int k = 0; k < BPT; ++k) s += d.h[k];
-  if (threadIdx.x == 0) *t_out = -1;
+  if (threadIdx.x == 0) {
+    *t_out = -1;
+    *above_out = 0;
+  }
   int total;
   const int excl = block_exclusive_scan<NT>(s, scan_scratch, &total);
   if (excl < need && need <= excl + s) {
@@ -102,7 +105,9 @@ __device__ void find_two_digits(const DigitBins<NT>& d1, const DigitBins<NT>& d2
   }
   if (threadIdx.x == 0) {
     sh[0] = -1;
+    sh[1] = 0;
     sh[2] = -1;
+    sh[3] = 0;
   }
   unsigned long long tot;
   const unsigned long long ex = block_exclusive_scan64<NT>(
@@ -194,7 +199,8 @@ __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, in
     g0 += __popcll(bg);
     t0 += __popcll(bt);
   }
-  const int n = G + (T < need_ties ? T : need_ties);
+  const int ties = T < need_ties ? T : need_ties;
+  const int n = G + (ties > 0 ? ties : 0);
   return n < K ? n : K;
 }
 

@@ -304,8 +304,12 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   const DigitBins<kSelNT> bins1 = load_digit_bins<kSelNT>(h1);
   const DigitBins<kSelNT> bins2 = load_digit_bins<kSelNT>(h2);
   find_two_digits<kSelNT>(bins1, bins2, K, scan64, sh);
-  const uint32_t tau = ((uint32_t)sh[0] << 11) | (uint32_t)sh[2];
-  const int need_ties = K - sh[1] - sh[3];
+  // both digits exist whenever the histograms hold the sequence's n > K
+  // entries; if they do not (a workspace that was not zeroed), nothing is
+  // selected
+  const bool have_tau = sh[0] >= 0 && sh[2] >= 0;
+  const uint32_t tau = have_tau ? ((uint32_t)sh[0] << 11) | (uint32_t)sh[2] : 0xFFFFFFFFu;
+  const int need_ties = have_tau ? K - sh[1] - sh[3] : 0;
 
   int cmax = 0, off = 0;
   if (few) {
@@ -366,7 +370,8 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
         ++t;
       }
     }
-    const int nsel = G + (T < need_ties ? T : need_ties);
+    const int ties = T < need_ties ? T : need_ties;
+    const int nsel = G + (ties > 0 ? ties : 0);
     written = nsel < K ? nsel : K;
   } else {
     // ---- general: concatenate the slot lists (offsets first)
