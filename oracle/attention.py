@@ -74,3 +74,22 @@ def dense_reference(q_bits: np.ndarray, sigma: float, x: np.ndarray):
     k = k.expand(1, q.shape[1], -1, -1).contiguous()
     o = torch.nn.functional.scaled_dot_product_attention(q, k, k, scale=float(sigma))
     return o[0, :, 0, :].numpy()
+
+
+def lse_merge(outs, lses) -> tuple[np.ndarray, np.ndarray]:
+    """Merge attention results over disjoint key sets (one per shard): with
+    M = max_s lse_s, w_s = exp(lse_s - M), the result is
+    o = sum_s w_s o_s / sum_s w_s and lse = M + ln sum_s w_s.  A part with no
+    keys (lse = -inf) has weight 0; if every part is empty, o = 0 and
+    lse = -inf.  Exact in real arithmetic: o_s = sum_j e^(l_j) x_j / e^(lse_s)."""
+    outs = [np.asarray(o, dtype=np.float64) for o in outs]
+    lses = np.stack([np.asarray(l, dtype=np.float64) for l in lses])      # [n, H]
+    M = lses.max(axis=0)
+    safe = np.where(np.isfinite(M), M, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - safe), 0.0)             # [n, H]
+    z = w.sum(axis=0)
+    o = sum(w[s][:, None] * outs[s] for s in range(len(outs)))
+    o = np.where(z[:, None] > 0, o / np.where(z > 0, z, 1.0)[:, None], 0.0)
+    lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    return o, lse
+

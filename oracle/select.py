@@ -69,3 +69,39 @@ def reindex(pool: np.ndarray, pool_count: int, scores_of_pool: np.ndarray,
 def reuse(idx: np.ndarray, count: int) -> tuple[np.ndarray, int]:
     """Reuse layer: the owner's (or the Reindex layer's) selection, unchanged."""
     return np.array(idx, copy=True), int(count)
+
+
+# ---------------------------------------------------------------- sharding
+# Context sharding of one long sequence (one shard per device, contiguous page
+# ranges): each shard ranks its own candidates under the same total order and
+# keeps its local Top-K; the global Top-K is then the Top-K of the union of the
+# local lists.  This holds because the order is total: an entry of the global
+# Top-K is beaten by fewer than K entries overall, hence by fewer than K in its
+# own shard, so it is in that shard's local list.  (The pages do not describe
+# sharding; this is the reading of the method's selection rule applied to a
+# partition of the candidates.)
+
+def topk_range(scores: np.ndarray, L: int, K: int, p_begin: int,
+               p_end: int) -> tuple[np.ndarray, int, np.ndarray]:
+    """Shard-local selection over candidates p_begin <= p < min(p_end, L-128),
+    ranked as in ``topk``.  Returns (positions ascending, padded with -1 to K;
+    count; the scores of those positions, 0 past the count)."""
+    hi = min(p_end, max(0, L - WINDOW))
+    pos = np.arange(p_begin, hi) if hi > p_begin else np.zeros(0, dtype=np.int64)
+    order = rank_order(scores[pos], pos)
+    idx, c = _emit(pos[order[:min(K, pos.size)]], K)
+    sc = np.zeros(K, dtype=np.int64)
+    sc[:c] = np.asarray(scores)[idx[:c]]
+    return idx, c, sc
+
+
+def merge_topk(parts, K: int) -> tuple[np.ndarray, int]:
+    """Global selection from shard-local lists over disjoint position sets:
+    ``parts`` holds (positions, count, scores) per shard; the union is ranked
+    by (score desc, position asc), the first min(K, total) kept, emitted
+    ascending and padded with -1."""
+    pos = np.concatenate([np.asarray(p[0][:p[1]], dtype=np.int64) for p in parts])
+    sc = np.concatenate([np.asarray(p[2][:p[1]], dtype=np.int64) for p in parts])
+    order = rank_order(sc, pos)
+    return _emit(pos[order[:min(K, pos.size)]], K)
+
