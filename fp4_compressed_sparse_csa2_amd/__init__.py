@@ -12,10 +12,13 @@ from ._lib import (  # noqa: F401
     Csa2Error,
     Workspace,
     index_topk,
+    index_topk_range,
     lib,
+    lse_merge,
     page_bytes,
     quantize_append,
     reindex,
     sparse_decode,
+    topk_merge,
     workspace_init,
 )

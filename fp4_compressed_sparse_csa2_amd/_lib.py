@@ -66,6 +66,14 @@ def lib() -> ctypes.CDLL:
             "csa2_sparse_decode": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, ctypes.c_float, _c_vp,
                                                   _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
                                                   _c_vp]),
+            "csa2_index_topk_range": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
+                                                     _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                                     _c_vp]),
+            "csa2_topk_merge_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+            "csa2_topk_merge": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
+                                               _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+            "csa2_lse_merge": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                              _c_vp, _c_vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -242,21 +250,23 @@ def reindex(cache: Cache, q_idx: torch.Tensor, pool: torch.Tensor, pool_count: t
 
 
 def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_scale: float,
-                  idx: torch.Tensor, idx_count: torch.Tensor, swa: torch.Tensor,
+                  idx: torch.Tensor, idx_count: torch.Tensor, swa: torch.Tensor | None,
                   ws: Workspace, out: torch.Tensor | None = None,
                   lse: torch.Tensor | None = None, want_lse: bool = True):
     """Merged sparse attention.  q bf16 [B, H, D]; idx int32 [B, K]; swa bf16
-    [B, 128, D].  Returns (out fp32 [B, H, D], lse fp32 [B, H] or None)."""
+    [B, 128, D], or None for no window rows (a context shard without the
+    tail).  Returns (out fp32 [B, H, D], lse fp32 [B, H] or None)."""
     dev, B, D = cache.device, cache.batch, cache.head_dim
     q = _as_u16(q)
-    swa = _as_u16(swa)
+    swa = None if swa is None else _as_u16(swa)
     H = q.shape[1]
     K = idx.shape[1]
     _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
     _need(q, "q", torch.uint16, dev, (B, H, D))
     _need(idx, "idx", torch.int32, dev, (B, K))
     _need(idx_count, "idx_count", torch.int32, dev, (B,))
-    _need(swa, "swa", torch.uint16, dev, (B, WINDOW, D))
+    if swa is not None:
+        _need(swa, "swa", torch.uint16, dev, (B, WINDOW, D))
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, (B, H, D))
@@ -270,7 +280,87 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
     w = ws.get(nbytes)
     _check(lib().csa2_sparse_decode(ctypes.byref(cache.struct), ctx_len.data_ptr(), H,
                                     q.data_ptr(), float(softmax_scale), idx.data_ptr(),
-                                    idx_count.data_ptr(), K, swa.data_ptr(), out.data_ptr(),
+                                    idx_count.data_ptr(), K, _ptr(swa), out.data_ptr(),
                                     _ptr(lse), w.data_ptr(), w.numel(), _stream(dev)),
            "csa2_sparse_decode")
     return out, lse
+
+
+# ------------------------------------------------------------------ sharding
+def index_topk_range(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
+                     K: int, p_begin: int, p_end: int, ws: Workspace,
+                     out_idx: torch.Tensor | None = None, out_count: torch.Tensor | None = None,
+                     out_sel_scores: torch.Tensor | None = None):
+    """Full-layer selection over candidates p_begin <= p < min(p_end, L-128)
+    (p_begin a multiple of 64).  Returns (idx [B, K], count [B], scores of the
+    selected [B, K])."""
+    dev, B = cache.device, cache.batch
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_sel_scores is None:
+        out_sel_scores = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    _need(out_sel_scores, "out_sel_scores", torch.int32, dev, (B, K))
+    nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
+    if nbytes == 0:
+        raise Csa2Error(f"index_topk_range: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_index_topk_range(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
+                                       q_idx.data_ptr(), K, p_begin, p_end, out_idx.data_ptr(),
+                                       out_count.data_ptr(), out_sel_scores.data_ptr(),
+                                       w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_index_topk_range")
+    return out_idx, out_count, out_sel_scores
+
+
+def topk_merge(idx: torch.Tensor, scores: torch.Tensor, counts: torch.Tensor, K: int,
+               ws: Workspace, out_idx: torch.Tensor | None = None,
+               out_count: torch.Tensor | None = None, out_sel_scores: torch.Tensor | None = None):
+    """Top-K of shard selections: idx / scores int32 [n, B, K_in] (ascending,
+    disjoint, parts in ascending position order), counts int32 [n, B].
+    Returns (idx [B, K], count [B], scores [B, K])."""
+    n, B, K_in = idx.shape
+    dev = idx.device
+    _need(idx, "idx", torch.int32, dev, (n, B, K_in))
+    _need(scores, "scores", torch.int32, dev, (n, B, K_in))
+    _need(counts, "counts", torch.int32, dev, (n, B))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_sel_scores is None:
+        out_sel_scores = torch.empty((B, K), dtype=torch.int32, device=dev)
+    nbytes = lib().csa2_topk_merge_workspace_size(B, n, K_in, K)
+    if nbytes == 0:
+        raise Csa2Error(f"topk_merge: unsupported sizes n={n} B={B} K_in={K_in} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_topk_merge(B, n, K_in, idx.data_ptr(), scores.data_ptr(), counts.data_ptr(),
+                                 K, out_idx.data_ptr(), out_count.data_ptr(),
+                                 out_sel_scores.data_ptr(), w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_topk_merge")
+    return out_idx, out_count, out_sel_scores
+
+
+def lse_merge(outs: torch.Tensor, lses: torch.Tensor, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None):
+    """Merge attention parts: outs fp32 [n, B, H, D], lses fp32 [n, B, H].
+    Returns (out [B, H, D], lse [B, H])."""
+    n, B, H, D = outs.shape
+    dev = outs.device
+    _need(outs, "outs", torch.float32, dev, (n, B, H, D))
+    _need(lses, "lses", torch.float32, dev, (n, B, H))
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, (B, H, D))
+    _need(lse, "lse", torch.float32, dev, (B, H))
+    _check(lib().csa2_lse_merge(n, B, H, D, outs.data_ptr(), lses.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), _stream(dev)), "csa2_lse_merge")
+    return out, lse
+

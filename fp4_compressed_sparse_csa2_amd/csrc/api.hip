@@ -52,6 +52,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
 
 constexpr int32_t kMaxK = 65536;
 constexpr int32_t kMaxCtx = 1 << 24;
+constexpr int32_t kMaxParts = 64;
 
 }  // namespace
 
@@ -105,9 +106,59 @@ int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max
   if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
   const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
   if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
-  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, out_idx,
-                                        out_count, out_scores, ws,
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, 0, kMaxCtx,
+                                        out_idx, out_count, out_scores, nullptr, ws,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_topk_range(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                          const int8_t* q_idx, int32_t K, int32_t p_begin, int32_t p_end,
+                          int32_t* out_idx, int32_t* out_count, int32_t* out_sel_scores,
+                          void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q_idx == nullptr || out_count == nullptr) return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
+  if (p_begin < 0 || p_begin % CSA2_PAGE_TOKENS != 0 || p_end < p_begin) return CSA2_E_SHAPE;
+  const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, p_begin,
+                                        p_end, out_idx, out_count, nullptr, out_sel_scores, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_topk_merge_workspace_size(int32_t batch, int32_t n_parts, int32_t K_in, int32_t K) {
+  if (batch < 1 || n_parts < 1 || n_parts > kMaxParts || K_in < 0 || K_in > kMaxK || K < 0 ||
+      K > kMaxK || (int64_t)n_parts * K_in > kMaxK * 8 || K > n_parts * K_in)
+    return 0;
+  return csa2::topk_merge_ws_bytes(batch, n_parts, K_in, K);
+}
+
+int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                    const int32_t* scores, const int32_t* counts, int32_t K, int32_t* out_idx,
+                    int32_t* out_count, int32_t* out_sel_scores, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (counts == nullptr || out_count == nullptr) return CSA2_E_NULL;
+  if (K_in > 0 && (idx == nullptr || scores == nullptr)) return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (batch < 1 || n_parts < 1 || n_parts > kMaxParts || K_in < 0 || K_in > kMaxK || K < 0 ||
+      K > kMaxK || (int64_t)n_parts * K_in > kMaxK * 8 || K > n_parts * K_in)
+    return CSA2_E_SHAPE;
+  const size_t need = csa2::topk_merge_ws_bytes(batch, n_parts, K_in, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_topk_merge(batch, n_parts, K_in, idx, scores, counts, K, out_idx,
+                                        out_count, out_sel_scores, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
+                   const float* outs, const float* lses, float* out, float* lse, void* stream) {
+  if (outs == nullptr || lses == nullptr || out == nullptr) return CSA2_E_NULL;
+  if (n_parts < 1 || n_parts > kMaxParts || batch < 1 || H < 1 || H > 128) return CSA2_E_SHAPE;
+  if (!supported_d(head_dim)) return CSA2_E_UNSUPPORTED;
+  return status_of(csa2::run_lse_merge(n_parts, batch, H, head_dim, outs, lses, out, lse,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t csa2_reindex_workspace_size(int32_t batch, int32_t P, int32_t K) {
@@ -144,8 +195,7 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
                        float* lse, void* ws, size_t ws_bytes, void* stream) {
   int st = check_cache(cache);
   if (st != CSA2_OK) return st;
-  if (ctx_len == nullptr || q == nullptr || idx_count == nullptr || swa == nullptr ||
-      out == nullptr)
+  if (ctx_len == nullptr || q == nullptr || idx_count == nullptr || out == nullptr)
     return CSA2_E_NULL;
   if (K > 0 && idx == nullptr) return CSA2_E_NULL;
   if (H < 16 || H > 128 || H % 16 != 0) return CSA2_E_UNSUPPORTED;

@@ -27,13 +27,17 @@ static_assert(kPagesPerWave >= 1 && kChunkPages % (kBlock / 64) == 0, "whole pag
 
 constexpr int kCtrlHist1 = 0;                  // the top-digit histogram in the control words
 
+// Candidates of sequence b: positions p_begin <= p < min(p_end, L - 128);
+// entry i is position p_begin + i.
 __device__ __forceinline__ int seq_candidates(const int32_t* ctx_len, int b, int max_ctx,
-                                              int max_pages) {
+                                              int max_pages, int p_begin, int p_end) {
   int L = ctx_len[b];
   L = L < 0 ? 0 : L;
   L = L > max_ctx ? max_ctx : L;
   L = L > max_pages * kPage ? max_pages * kPage : L;
-  return L > kWindow ? L - kWindow : 0;
+  int hi = L > kWindow ? L - kWindow : 0;
+  hi = hi < p_end ? hi : p_end;
+  return hi > p_begin ? hi - p_begin : 0;
 }
 
 // ------------------------------------------------------------------ score
@@ -41,14 +45,14 @@ template <int DI>
 __global__ __launch_bounds__(kBlock) void index_score_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
     int max_pages, int keys_off, int page_bytes, const int32_t* __restrict__ ctx_len,
-    int max_ctx, const int8_t* __restrict__ q_idx, int K, int32_t* __restrict__ scores,
-    int32_t* __restrict__ out_scores, uint32_t* __restrict__ ctrl) {
+    int max_ctx, int p_begin, int p_end, const int8_t* __restrict__ q_idx, int K,
+    int32_t* __restrict__ scores, int32_t* __restrict__ out_scores, uint32_t* __restrict__ ctrl) {
   constexpr int LPP = DI / 16;        // lanes per position (16 key bytes each)
   constexpr int PPL = 64 / LPP;       // positions per 1 KB wave load
   __shared__ uint32_t hist[kBins];
 
   const int b = blockIdx.y;
-  const int n = seq_candidates(ctx_len, b, max_ctx, max_pages);
+  const int n = seq_candidates(ctx_len, b, max_ctx, max_pages, p_begin, p_end);
   const int chunk0 = blockIdx.x * kChunk;
   if (chunk0 >= n) return;
   const bool do_hist = K > 0 && n > K;
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
   __builtin_amdgcn_sched_barrier(0);     // the query goes out before the keys
-  const int32_t* pt = page_table + (size_t)b * max_pages;
+  const int32_t* pt = page_table + (size_t)b * max_pages + p_begin / kPage;
   int32_t* sc_row = scores + (size_t)b * row_stride(max_ctx);
   int32_t* user_row = out_scores ? out_scores + (size_t)b * max_ctx : nullptr;
   // after the lane-group sums, lane l keeps the score of page row ppos
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
     const int p = (lp0 + pi) * kPage + ppos;
     if (p < n) {
       sc_row[p] = keep;
-      if (user_row) user_row[p] = keep;
+      if (user_row) user_row[p_begin + p] = keep;
       if (do_hist) atomicAdd(&hist[score_key(keep) >> 11], 1u);
     }
     __builtin_amdgcn_sched_barrier(0);   // pages in arrival order
@@ -144,31 +148,37 @@ size_t index_topk_ws_bytes(int batch, int max_ctx, int /*K*/) {
 }
 
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
-                          const int8_t* q_idx, int K, int32_t* out_idx, int32_t* out_count,
-                          int32_t* out_scores, void* ws, hipStream_t st) {
+                          const int8_t* q_idx, int K, int p_begin, int p_end, int32_t* out_idx,
+                          int32_t* out_count, int32_t* out_scores, int32_t* out_sel_scores,
+                          void* ws, hipStream_t st) {
   const TopkWs w = topk_ws(c.batch, max_ctx);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + w.ctrl);
   int32_t* scores = reinterpret_cast<int32_t*>(base + w.scores);
   const PageLayout lay = page_layout(c.D, c.Di);
-  const int n_chunks = (max_ctx + kChunk - 1) / kChunk;
+  int hi = max_ctx > kWindow ? max_ctx - kWindow : 0;   // most candidates a sequence can have
+  hi = hi < p_end ? hi : p_end;
+  const int max_entries = hi > p_begin ? hi - p_begin : 0;
+  const int n_chunks = (max_entries + kChunk - 1) / kChunk;
   const dim3 grid(n_chunks > 0 ? n_chunks : 1, c.batch);
   if (c.Di == 128)
     hipLaunchKernelGGL(index_score_kernel<128>, grid, dim3(kBlock), 0, st,
                        (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, q_idx, K, scores,
-                       out_scores, ctrl);
+                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx, K,
+                       scores, out_scores, ctrl);
   else
     hipLaunchKernelGGL(index_score_kernel<64>, grid, dim3(kBlock), 0, st,
                        (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, q_idx, K, scores,
-                       out_scores, ctrl);
+                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx, K,
+                       scores, out_scores, ctrl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelectArgs a;
   a.ctx_len = ctx_len;
   a.max_ctx = max_ctx;
   a.max_pages = c.max_pages;
+  a.p_begin = p_begin;
+  a.p_end = p_end;
   a.pool = nullptr;
   a.pool_count = nullptr;
   a.P = 0;
@@ -181,7 +191,8 @@ hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ct
   a.chunk_counts = reinterpret_cast<uint32_t*>(base + w.counts);
   a.out_idx = out_idx;
   a.out_count = out_count;
-  return run_select(a, max_ctx > kWindow ? max_ctx - kWindow : 0, st);
+  a.out_sel_scores = out_sel_scores;
+  return run_select(a, max_entries, st);
 }
 
 }  // namespace csa2

@@ -24,9 +24,11 @@ hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st);
 // of a Full layer, i = position) or from pool_count (a Reindex layer's pool,
 // output id = pool[b][i]).
 struct SelectArgs {
-  const int32_t* ctx_len;     // Full layer: n_b = clamp(ctx_len[b]) - 128
+  const int32_t* ctx_len;     // Full layer: candidates p_begin <= p < min(p_end, L_b - 128)
   int max_ctx;
   int max_pages;
+  int p_begin;                // multiple of 64; entry i is position p_begin + i
+  int p_end;
   const int32_t* pool;        // Reindex layer (non-NULL): [batch][P]
   const int32_t* pool_count;
   int P;
@@ -39,6 +41,7 @@ struct SelectArgs {
   uint32_t* chunk_counts;     // [batch][kMaxSelChunks]
   int32_t* out_idx;           // [batch][K]
   int32_t* out_count;         // [batch]
+  int32_t* out_sel_scores;    // [batch][K] scores of the selected entries, or NULL
 };
 hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st);
 
@@ -48,13 +51,22 @@ hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, con
 
 size_t index_topk_ws_bytes(int batch, int max_ctx, int K);
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
-                          const int8_t* q_idx, int K, int32_t* out_idx, int32_t* out_count,
-                          int32_t* out_scores, void* ws, hipStream_t st);
+                          const int8_t* q_idx, int K, int p_begin, int p_end, int32_t* out_idx,
+                          int32_t* out_count, int32_t* out_scores, int32_t* out_sel_scores,
+                          void* ws, hipStream_t st);
 
 size_t reindex_ws_bytes(int batch, int P, int K);
 hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* pool,
                        const int32_t* pool_count, int P, int K, int32_t* out_idx,
                        int32_t* out_count, int32_t* out_scores, void* ws, hipStream_t st);
+
+size_t topk_merge_ws_bytes(int batch, int n_parts, int K_in, int K);
+hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
+                          const int32_t* scores, const int32_t* counts, int K, int32_t* out_idx,
+                          int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st);
+
+hipError_t run_lse_merge(int n_parts, int batch, int H, int D, const float* outs,
+                         const float* lses, float* out, float* lse, hipStream_t st);
 
 size_t sparse_decode_ws_bytes(int batch, int H, int D, int K);
 hipError_t run_sparse_decode(const CacheArgs& c, const int32_t* ctx_len, int H,

@@ -143,6 +143,8 @@ hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* p
   a.ctx_len = nullptr;
   a.max_ctx = 0;
   a.max_pages = c.max_pages;
+  a.p_begin = 0;
+  a.p_end = 0;
   a.pool = pool;
   a.pool_count = pool_count;
   a.P = P;
@@ -155,6 +157,7 @@ hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* p
   a.chunk_counts = reinterpret_cast<uint32_t*>(base + w.counts);
   a.out_idx = out_idx;
   a.out_count = out_count;
+  a.out_sel_scores = nullptr;
   return run_select(a, P, st);
 }
 

@@ -144,6 +144,12 @@ __device__ void find_two_digits(const DigitBins<NT>& d1, const DigitBins<NT>& d2
   __syncthreads();
 }
 
+// The int32 score of a biased key (score_key's inverse; the folded top key
+// is the one score 2^21).
+__device__ __forceinline__ int32_t key_score(uint32_t key) {
+  return key == 0x3FFFFFu ? (1 << 21) : (int32_t)key - kKeyBias;
+}
+
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -153,7 +159,8 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 //   get(f) -> uint2{key, id} for f < total, ids strictly ascending in f.
 //   key > tau: selected; key == tau: the first `need_ties` of them (lowest
 //   ids) are selected; key < tau: dropped.
-// Calls put(j, id) for the j-th selected entry (ascending ids), j < K, and
+// Calls put(j, c) for the j-th selected entry c = {key, id} (ascending ids),
+// j < K, and
 // returns the number selected (uniform).  Each wave takes one contiguous run
 // of candidates, counts its selections with ballots, and after one barrier
 // (the per-wave totals, `wave_tot`: NT/64 shared int2) places them with
@@ -192,9 +199,9 @@ __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, in
     const int gb = g0 + lanes_below(bg), tb = t0 + lanes_below(bt);   // before this entry
     if (gt) {
       const int slot = gb + (tb < need_ties ? tb : need_ties);
-      if (slot < K) put(slot, c.y);
+      if (slot < K) put(slot, c);
     } else if (tie) {
-      if (tb < need_ties && gb + tb < K) put(gb + tb, c.y);
+      if (tb < need_ties && gb + tb < K) put(gb + tb, c);
     }
     g0 += __popcll(bg);
     t0 += __popcll(bt);

@@ -51,18 +51,31 @@ __device__ __forceinline__ int sel_entries(const SelectArgs& a, int b) {
   L = L < 0 ? 0 : L;
   L = L > a.max_ctx ? a.max_ctx : L;
   L = L > a.max_pages * kPage ? a.max_pages * kPage : L;
-  return L > kWindow ? L - kWindow : 0;
+  int hi = L > kWindow ? L - kWindow : 0;              // candidates end below the window
+  hi = hi < a.p_end ? hi : a.p_end;
+  return hi > a.p_begin ? hi - a.p_begin : 0;
 }
 
-// Output id of entry i: the position itself, or the pool's position.
+// Output id of entry i: its position (p_begin + i), or the pool's position.
 __device__ __forceinline__ int32_t sel_id(const SelectArgs& a, int b, uint32_t i) {
-  return a.pool != nullptr ? a.pool[(size_t)b * a.P + i] : (int32_t)i;
+  return a.pool != nullptr ? a.pool[(size_t)b * a.P + i] : a.p_begin + (int32_t)i;
+}
+
+// The j-th selected entry c = {key, entry} of sequence b: its id, and its
+// score when the caller asked for them.
+__device__ __forceinline__ void put_sel(const SelectArgs& a, int b, int j, uint2 c) {
+  a.out_idx[(size_t)b * a.K + j] = sel_id(a, b, c.y);
+  if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = key_score(c.x);
 }
 
 // K = 0 or every entry selected: the first min(K, n) entries in order, then -1.
 __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, int nt) {
   int32_t* out = a.out_idx + (size_t)b * a.K;
-  for (int i = threadIdx.x; i < a.K; i += nt) out[i] = i < n ? sel_id(a, b, (uint32_t)i) : -1;
+  const int32_t* row = a.scores + (size_t)b * a.stride;
+  for (int i = threadIdx.x; i < a.K; i += nt) {
+    out[i] = i < n ? sel_id(a, b, (uint32_t)i) : -1;
+    if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + i] = i < n ? row[i] : 0;
+  }
   if (threadIdx.x == 0) a.out_count[b] = n < a.K ? n : a.K;
 }
 
@@ -188,8 +201,11 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   int32_t* out = a.out_idx + (size_t)b * K;
   const int written = emit_in_order<kSelNT>(
       get, total, tau, need_ties, K, wave_tot,
-      [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
-  for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
+      [&](int j, uint2 c) { put_sel(a, b, j, c); });
+  for (int j = written + tid; j < K; j += kSelNT) {
+    out[j] = -1;
+    if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
+  }
   if (tid == 0) a.out_count[b] = written;
   for (int i = tid; i < kBins; i += kSelNT) h1[i] = 0u;     // ready for the next call
 }
@@ -363,10 +379,10 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     for (int k = 0; k < spl; ++k) {
       if ((gtm >> k) & 1u) {
         const int slot = g + (t < need_ties ? t : need_ties);
-        if (slot < K) out[slot] = sel_id(a, b, e[k].y);
+        if (slot < K) put_sel(a, b, slot, e[k]);
         ++g;
       } else if ((tiem >> k) & 1u) {
-        if (t < need_ties && g + t < K) out[g + t] = sel_id(a, b, e[k].y);
+        if (t < need_ties && g + t < K) put_sel(a, b, g + t, e[k]);
         ++t;
       }
     }
@@ -404,9 +420,12 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       return cand_row[(size_t)lo * kFiltChunk + (f - offs[lo])];
     };
     written = emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot,
-                                    [&](int j, uint32_t id) { out[j] = sel_id(a, b, id); });
+                                    [&](int j, uint2 c) { put_sel(a, b, j, c); });
   }
-  for (int j = written + tid; j < K; j += kSelNT) out[j] = -1;
+  for (int j = written + tid; j < K; j += kSelNT) {
+    out[j] = -1;
+    if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
+  }
   if (tid == 0) a.out_count[b] = written;
   for (int i = tid; i < 2 * kBins; i += kSelNT) h1[i] = 0u;   // both histograms, for the next call
 }

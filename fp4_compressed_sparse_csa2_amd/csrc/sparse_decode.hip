@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     fa = (split - kWinTiles) * split_tiles;
     fb0 = min(fa + split_tiles, tiles_k);
   }
+  if (swa == nullptr) wb0 = wa;                          // no window rows at all
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
 
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const int32_t* idx_row = idx + (size_t)b * K;
-  const uint16_t* swa_b = swa + (size_t)b * kWindow * D;
+  const uint16_t* swa_b = swa != nullptr ? swa + (size_t)b * kWindow * D : nullptr;
 
   // ---- prologue: every load is issued before any result is used
   // window rows by ring slot: window tile t holds slots 64t .. 64t+63 (the
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
   const int L = L_raw < 0 ? 0 : (L_raw > max_pages * kPage ? max_pages * kPage : L_raw);
   const int n_glob = L > kWindow ? L - kWindow : 0;     // selectable positions
   const int cnt = cnt_raw < 0 ? 0 : (cnt_raw > K ? K : cnt_raw);
-  const int n_win = L < kWindow ? L : kWindow;
+  const int n_win = swa == nullptr ? 0 : (L < kWindow ? L : kWindow);
   const int wb = min(wb0, (n_win + kTile - 1) / kTile);  // tiles that hold tokens
   const int fb = min(fb0, (cnt + kTile - 1) / kTile);
   const int nf = fb > fa ? fb - fa : 0;

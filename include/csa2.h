@@ -219,9 +219,13 @@ int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx,
  * swa          device uint16 [batch][128][D] bf16 ring of this layer; its
  *              values must be finite with magnitude <= 65504 (the window rows
  *              run through fp16 MFMA operands; magnitudes below 2^-14 keep
- *              fp16 subnormal precision).
+ *              fp16 subnormal precision).  NULL: no window rows (a context
+ *              shard that holds none of the last 128 positions, see below).
  * out          device float [batch][H][D]; lse device float [batch][H] or NULL.
  * ws           workspace of csa2_sparse_decode_workspace_size(batch, H, D, K).
+ * Selected positions whose page-table entry lies outside [0, num_pages)
+ * are skipped, so a shard's cache view with -1 for the pages it does not
+ * hold attends over its own rows only.
  * Errors: CSA2_E_NULL, CSA2_E_UNSUPPORTED (D, H), CSA2_E_SHAPE (K, batch),
  *         CSA2_E_WORKSPACE.
  */
@@ -231,6 +235,74 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
                        const int32_t* idx, const int32_t* idx_count, int32_t K,
                        const uint16_t* swa, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Context sharding of long sequences (several devices each holding a
+ * contiguous range of a sequence's pages).  Each shard selects among its own
+ * candidates under the Full layer's order; csa2_topk_merge turns the shard
+ * lists into the one-device selection (exactly: an entry of the global Top-K
+ * is beaten by fewer than K entries overall, hence by fewer than K in its
+ * shard); each shard attends over the selected rows it holds (the tail shard
+ * also over the window) and csa2_lse_merge combines the parts, which is the
+ * one softmax over the union.  Selection rule: neodrop.ai V4.1-Flash report,
+ * 架构拆解 item 2; one softmax over the merged caches: infernews.com V4.1
+ * Flash page, section 2.
+ */
+
+/*
+ * csa2_index_topk_range -- Full-layer selection restricted to the candidate
+ * positions p_begin <= p < min(p_end, L - 128) of every sequence (entries,
+ * order, tie rule and output form as csa2_index_topk).
+ *
+ * p_begin, p_end  (host) p_begin a multiple of 64, p_begin <= p_end.
+ * out_sel_scores  device int32 [batch][K] or NULL: the score of each
+ *                 selected position (aligned with out_idx), 0 past the count.
+ * ws              workspace of csa2_index_topk_workspace_size(batch, max_ctx, K).
+ * Errors: as csa2_index_topk, and CSA2_E_SHAPE for the range.
+ */
+int csa2_index_topk_range(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                          const int8_t* q_idx, int32_t K, int32_t p_begin, int32_t p_end,
+                          int32_t* out_idx, int32_t* out_count, int32_t* out_sel_scores,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_topk_merge -- the Top-K of n_parts shard selections of each sequence.
+ *
+ * idx      device int32 [n_parts][batch][K_in]: part s's positions of
+ *          sequence b, strictly ascending; the parts of a sequence hold
+ *          disjoint positions, in ascending order of part (part s below part
+ *          s + 1), as csa2_index_topk_range returns them for ascending ranges.
+ * scores   device int32 [n_parts][batch][K_in]: their scores.
+ * counts   device int32 [n_parts][batch]: entries per part (clamped to
+ *          [0, K_in]).
+ * Output: out_idx[b] = the first min(K, total) of the union in (score
+ * descending, position ascending) order, ascending, -1 padded to K;
+ * out_count[b]; out_sel_scores (device int32 [batch][K] or NULL) their scores.
+ * Limits: 1 <= n_parts <= 64, 0 <= K_in <= 65536, n_parts*K_in <= 524288,
+ *         0 <= K <= min(65536, n_parts*K_in).
+ * ws       workspace of csa2_topk_merge_workspace_size(batch, n_parts, K_in, K).
+ * Errors: CSA2_E_NULL, CSA2_E_SHAPE, CSA2_E_WORKSPACE.
+ */
+size_t csa2_topk_merge_workspace_size(int32_t batch, int32_t n_parts, int32_t K_in, int32_t K);
+int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                    const int32_t* scores, const int32_t* counts, int32_t K,
+                    int32_t* out_idx, int32_t* out_count, int32_t* out_sel_scores,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_lse_merge -- merge attention results over disjoint key sets.
+ * For each row r = (b, h): M = max_s lses[s][r], w_s = exp(lses[s][r] - M)
+ * (0 when lses[s][r] = -inf), out[r] = sum_s w_s outs[s][r] / sum_s w_s,
+ * lse[r] = M + ln sum_s w_s (out = 0, lse = -inf when every part is empty).
+ *
+ * outs  device float [n_parts][batch][H][D]; lses device float [n_parts][batch][H]
+ *       (csa2_sparse_decode's out and lse of each part).
+ * out   device float [batch][H][D]; lse device float [batch][H] or NULL.
+ * Limits: 1 <= n_parts <= 64, 1 <= H <= 128, D = head_dim in {128, 256, 512}.
+ * Errors: CSA2_E_NULL, CSA2_E_SHAPE, CSA2_E_UNSUPPORTED.
+ */
+int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
+                   const float* outs, const float* lses, float* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

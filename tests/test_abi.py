@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -73,3 +73,25 @@ def test_validation_codes(L):
     # sparse_decode: H not a multiple of 16, null output
     assert L.csa2_sparse_decode(P(c), 1, 24, 1, 1.0, 1, 1, 8, 1, 1, None, 1, 1 << 30, None) == -3
     assert L.csa2_sparse_decode(P(c), 1, 16, 1, 1.0, 1, 1, 8, 1, None, None, 1, 1 << 30, None) == -1
+
+
+def test_shard_calls_validate_before_launch(L):
+    c = _cache()
+    P = ctypes.pointer
+    # index_topk_range: p_begin not page-aligned, p_end below p_begin, null output
+    assert L.csa2_index_topk_range(P(c), 1, 100, 1, 8, 32, 200, 1, 1, None, 1, 1 << 30, None) == -2
+    assert L.csa2_index_topk_range(P(c), 1, 100, 1, 8, 64, 10, 1, 1, None, 1, 1 << 30, None) == -2
+    assert L.csa2_index_topk_range(P(c), 1, 100, 1, 8, 0, 10, None, 1, None, 1, 1 << 30, None) == -1
+    # topk_merge: sizes and workspace
+    assert L.csa2_topk_merge_workspace_size(8, 4, 2048, 2048) > 0
+    assert L.csa2_topk_merge_workspace_size(8, 0, 2048, 2048) == 0
+    assert L.csa2_topk_merge_workspace_size(8, 65, 16, 16) == 0
+    assert L.csa2_topk_merge_workspace_size(8, 2, 16, 40) == 0          # K > n * K_in
+    assert L.csa2_topk_merge(8, 2, 16, 1, 1, 1, 40, 1, 1, None, 1, 1 << 30, None) == -2
+    assert L.csa2_topk_merge(8, 2, 16, 1, 1, None, 8, 1, 1, None, 1, 1 << 30, None) == -1
+    assert L.csa2_topk_merge(8, 2, 16, 1, 1, 1, 8, 1, 1, None, None, 0, None) == -4
+    # lse_merge: null input, unsupported D, part count
+    assert L.csa2_lse_merge(2, 8, 64, 512, None, 1, 1, None, None) == -1
+    assert L.csa2_lse_merge(2, 8, 64, 384, 1, 1, 1, None, None) == -3
+    assert L.csa2_lse_merge(0, 8, 64, 512, 1, 1, 1, None, None) == -2
+
