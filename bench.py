@@ -81,6 +81,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE counter runs of --counter-run "
                          "into profiles/traffic.json and exit")
+    ap.add_argument("--dcp", type=int, default=0, metavar="N",
+                    help="instead of the headline bench: the 1M-token sequence cut over N "
+                         "emulated devices (range Top-K per shard, merge, shard decodes, LSE "
+                         "merge) against the one-device step, one JSON line")
     return ap.parse_args()
 
 
@@ -122,7 +126,7 @@ def measured_traffic(kernel: str):
 
 # ------------------------------------------------------------------ GPU side
 class Setup:
-    def __init__(self, replicas: int):
+    def __init__(self, replicas: int, workload: str = WORKLOAD):
         import torch
 
         import fp4_compressed_sparse_csa2_amd as csa2
@@ -130,7 +134,7 @@ class Setup:
 
         self.torch, self.csa2, self.gen = torch, csa2, gen
         dev = self.dev = torch.device("cuda:0")
-        wl = self.wl = gen.WORKLOADS[WORKLOAD]
+        wl = self.wl = gen.WORKLOADS[workload]
         B, L, D, Di = wl.B, wl.L, wl.D, wl.Di
         self.lens = gen.ctx_lens(wl)
         pt, npages = gen.page_table(wl, self.lens)
@@ -382,6 +386,108 @@ def gpu_bench(args, S: Setup):
     return wall, ev_ms, calls, parity, spread
 
 
+# ------------------------------------------------------------------ sharded context
+def shard_bounds(L: int, n: int) -> list:
+    """n page-aligned ascending position ranges covering [0, L); the last is open."""
+    pages = -(-L // 64)
+    cuts = [int(round(pages * i / n)) * 64 for i in range(n)]
+    return [(cuts[i], cuts[i + 1] if i + 1 < n else 1 << 24) for i in range(n)]
+
+
+def dcp_bench(args) -> dict:
+    """The 1M-token sequence cut into N page-aligned shards, one per emulated
+    device: each shard's range Top-K (with scores), the merge of the shard
+    lists, each shard's attention over the merged selection through a page
+    table that holds only its pages (the window on the tail shard), and the
+    LSE merge; against the one-device index_topk + sparse_decode on the same
+    cache.  Calls are timed as graph replays over two cold cache replicas.
+    The emulated step adds the slowest shard's selection, the merge, the
+    slowest shard's decode and the LSE merge; the exchanges between devices
+    (an all-gather of N*K (score, position) pairs and a reduction of the
+    partial outputs) are not part of it."""
+    import torch
+    S = Setup(2, "b1_1m")
+    csa2, wl, dev = S.csa2, S.wl, S.dev
+    n, B, K, H, D = args.dcp, wl.B, wl.K, wl.H, wl.D
+    L = int(S.lens.max())
+    bounds = shard_bounds(L, n)
+    R = len(S.caches)
+    pidx = torch.empty((n, B, K), dtype=torch.int32, device=dev)
+    psc = torch.empty((n, B, K), dtype=torch.int32, device=dev)
+    pcnt = torch.empty((n, B), dtype=torch.int32, device=dev)
+    midx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    mcnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    msc = torch.empty((B, K), dtype=torch.int32, device=dev)
+    outs = torch.empty((n, B, H, D), dtype=torch.float32, device=dev)
+    lses = torch.empty((n, B, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_t = [csa2.Workspace(dev) for _ in range(n)]
+    ws_d = [csa2.Workspace(dev) for _ in range(n)]
+    ws_m = csa2.Workspace(dev)
+    views = []
+    for r in range(R):
+        vs = []
+        for s, (a, e) in enumerate(bounds):
+            pt = S.caches[r].page_table.clone()
+            own = torch.zeros(pt.shape[1], dtype=torch.bool, device=dev)
+            own[a // 64: min(pt.shape[1], -(-e // 64))] = True
+            pt[:, ~own] = -1
+            vs.append(csa2.Cache(S.caches[r].pages, pt.contiguous(), D, wl.Di))
+        views.append(vs)
+
+    def topk_fn(s):
+        a, e = bounds[s]
+        return lambda r: csa2.index_topk_range(S.caches[r], S.ctx, S.max_ctx, S.q_idx, K, a, e,
+                                               ws_t[s], out_idx=pidx[s], out_count=pcnt[s],
+                                               out_sel_scores=psc[s])
+
+    def merge(r):
+        csa2.topk_merge(pidx, psc, pcnt, K, ws_m, out_idx=midx, out_count=mcnt, out_sel_scores=msc)
+
+    def dec_fn(s):
+        return lambda r: csa2.sparse_decode(views[r][s], S.ctx, S.q, S.sigma, midx, mcnt,
+                                            S.rings[r] if s == n - 1 else None, ws_d[s],
+                                            out=outs[s], lse=lses[s])
+
+    def lsem(r):
+        csa2.lse_merge(outs, lses, out=out, lse=lse)
+
+    for r in range(R):                        # eager pass: workspaces, results
+        for s in range(n):
+            topk_fn(s)(r)
+        merge(r)
+        for s in range(n):
+            dec_fn(s)(r)
+        lsem(r)
+        S.index_topk(r)
+        S.decode(r)
+    torch.cuda.synchronize()
+    same_idx = bool(torch.equal(midx, S.idx) and torch.equal(mcnt, S.cnt))
+    out_err = float((out - S.out).abs().max())
+    t_topk = [time_call(S, topk_fn(s), R) for s in range(n)]
+    t_merge = time_call(S, merge, R)
+    t_dec = [time_call(S, dec_fn(s), R) for s in range(n)]
+    t_lse = time_call(S, lsem, R)
+    t_one_topk = time_call(S, S.index_topk, R)
+    t_one_dec = time_call(S, S.decode, R)
+    emulated = max(t_topk) + t_merge + max(t_dec) + t_lse
+    one = t_one_topk + t_one_dec
+    return {"metric": "context-sharded decode step, emulated on one GPU",
+            "workload": f"b1_1m: batch 1, ctx {L}, 64 heads, latent 512 FP4, indexer dim 128, "
+                        f"Top-K {K}, SWA 128; {n} page-aligned shards",
+            "shards": [list(b) for b in bounds],
+            "range_topk_us": t_topk, "merge_us": t_merge, "shard_decode_us": t_dec,
+            "lse_merge_us": t_lse, "emulated_step_us": emulated,
+            "one_device": {"index_topk_us": t_one_topk, "sparse_decode_us": t_one_dec,
+                           "step_us": one},
+            "speedup_vs_one_device": one / emulated,
+            "merged_indices_equal_one_device": same_idx,
+            "merged_out_max_abs_diff_vs_one_device": out_err,
+            "excluded": "device-to-device exchanges (all-gather of N*K pairs, reduction of "
+                        "the partial outputs)"}
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(S: Setup, seconds: float):
     """The oracle's decode step (append of the new token, indexer scores,
@@ -524,6 +630,9 @@ def main() -> int:
         return 2
     if args.counter_run:
         return counter_run(args)
+    if args.dcp:
+        print(json.dumps(dcp_bench(args)), flush=True)
+        return 0
     S = Setup(args.replicas)
     wl = S.wl
     wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
