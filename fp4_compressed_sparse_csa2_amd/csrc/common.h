@@ -32,6 +32,8 @@ __device__ __forceinline__ uint32_t score_key(int s) {
   return k > 0x3FFFFFu ? 0x3FFFFFu : k;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------ lanes
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 

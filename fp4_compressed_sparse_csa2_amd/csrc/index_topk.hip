@@ -77,16 +77,20 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
   }
   // then every key load, unconditionally (a page that is not live reads
   // page 0, which always exists, and is skipped), so that page pi's compute
-  // waits only for its own loads
+  // waits only for its own loads.  The keys are read once per call:
+  // non-temporal loads keep them from evicting what the next kernels reuse.
   uint4 v[kPagesPerWave][LPP];
   bool live[kPagesPerWave];
 #pragma unroll
   for (int pi = 0; pi < kPagesPerWave; ++pi) {
     live[pi] = pg[pi] >= 0 && pg[pi] < num_pages;
-    const uint4* kp = reinterpret_cast<const uint4*>(
+    const u32x4* kp = reinterpret_cast<const u32x4*>(
         pages + (size_t)(live[pi] ? pg[pi] : 0) * page_bytes + keys_off);
 #pragma unroll
-    for (int j = 0; j < LPP; ++j) v[pi][j] = kp[j * 64 + lane];
+    for (int j = 0; j < LPP; ++j) {
+      const u32x4 t = __builtin_nontemporal_load(kp + j * 64 + lane);
+      v[pi][j] = make_uint4(t.x, t.y, t.z, t.w);
+    }
     __builtin_amdgcn_sched_barrier(0);   // keep the pages' loads in page order
   }
   if (do_hist) {                         // while the keys are on their way

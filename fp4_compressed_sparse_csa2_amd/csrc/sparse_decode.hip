@@ -503,11 +503,13 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     return;
   }
 
-  // ---- split partials: (m, l) per head and the unnormalised O
+  // ---- split partials: (m, l) per head and the unnormalised O, stored
+  // non-temporally (read once, by the combine kernel)
   const size_t prow = ((size_t)unit * n_splits + split) * kHG + lc;   // partial row of head lc
   float* orow = part_o + prow * D + wave * DQ + 4 * lg;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<floatx4*>(orow + nb * 16) = acc[nb];
+  for (int nb = 0; nb < NB; ++nb)
+    __builtin_nontemporal_store(acc[nb], reinterpret_cast<floatx4*>(orow + nb * 16));
   if (wave == 0 && lg == 0) part_ml[prow] = make_float2(m_q, l_tot);
 }
 
@@ -539,7 +541,9 @@ __global__ __launch_bounds__(kBlock) void sparse_combine_kernel(
     for (int i = 0; i < SB; ++i) {
       if (s0 + i < n_splits) {
         ml[i] = part_ml[(ubase + s0 + i) * kHG + h];
-        x[i] = src[(s0 + i) * ostep];
+        const floatx4 t =       // partials are read once: non-temporal
+            __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + (s0 + i) * ostep));
+        x[i] = make_float4(t.x, t.y, t.z, t.w);
       } else {
         ml[i] = make_float2(-INFINITY, 0.f);
         x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
