@@ -380,9 +380,19 @@ def gpu_bench(args, S: Setup):
         torch.cuda.synchronize()
         per_step.append(e0.elapsed_time(e1) * 1e3 / S_big)
     warm_us = time_call(S, S.step, 1)
+    # bounded replay: rebuild every window ring from the bf16 tokens of the
+    # last 128 positions (csa2_quantize_append of B x 128 tokens, ring written)
+    B, W = S.wl.B, 128
+    seq = torch.arange(B, dtype=torch.int32, device=S.dev).repeat_interleave(W)
+    pos = torch.cat([torch.arange(int(L) - W, int(L), dtype=torch.int32, device=S.dev)
+                     for L in S.lens])
+    tok = torch.stack([S.rings[0][b][pos[b * W:(b + 1) * W] % W] for b in range(B)]).reshape(B * W, -1)
+    restore_us = time_call(S, lambda r: S.csa2.quantize_append(S.caches[r], tok, seq, pos,
+                                                               swa=S.rings[r]), R)
     spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
               "p90": float(np.percentile(per_step, 90)), "warm_one_replica": warm_us,
-              "replays": len(per_step), "steps_per_replay": S_big}
+              "replays": len(per_step), "steps_per_replay": S_big,
+              "window_restore_us": restore_us}
     return wall, ev_ms, calls, parity, spread
 
 

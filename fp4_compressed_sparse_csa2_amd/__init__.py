@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     page_bytes,
     quantize_append,
     reindex,
+    restore_window,
     sparse_decode,
     topk_merge,
     workspace_init,

@@ -364,3 +364,30 @@ def lse_merge(outs: torch.Tensor, lses: torch.Tensor, out: torch.Tensor | None =
                                 lse.data_ptr(), _stream(dev)), "csa2_lse_merge")
     return out, lse
 
+
+# ------------------------------------------------------------------ replay
+def restore_window(cache: Cache, swa: torch.Tensor, tokens: torch.Tensor, lens) -> None:
+    """Rebuild a layer's window ring after it was dropped, from the bf16 tokens
+    of the last min(L_b, 128) positions of every sequence: tokens [B, 128, D]
+    (bf16), row j of sequence b holding position L_b - 128 + j (rows of
+    positions below 0 are ignored); lens: the host lengths L_b.  The tokens
+    are re-appended with csa2_quantize_append (window ring written, indexer
+    keys untouched); their FP4 rows are rewritten with the bytes they already
+    hold, since the quantisation is a function of the token alone."""
+    dev, B, D = cache.device, cache.batch, cache.head_dim
+    tokens = _as_u16(tokens)
+    _need(tokens, "tokens", torch.uint16, dev, (B, WINDOW, D))
+    lens = [int(v) for v in lens]
+    if len(lens) != B:
+        raise ValueError(f"lens must hold {B} lengths")
+    rows, seq, pos = [], [], []
+    for b, L in enumerate(lens):
+        w = min(max(L, 0), WINDOW)
+        if w:
+            rows.append(tokens[b, WINDOW - w:])
+            seq.append(torch.full((w,), b, dtype=torch.int32, device=dev))
+            pos.append(torch.arange(L - w, L, dtype=torch.int32, device=dev))
+    if rows:
+        quantize_append(cache, torch.cat(rows).contiguous(), torch.cat(seq), torch.cat(pos),
+                        swa=swa)
+
