@@ -396,6 +396,36 @@ def gpu_bench(args, S: Setup):
     return wall, ev_ms, calls, parity, spread
 
 
+def schedule_calls(S: Setup, n_layers: int = 20) -> dict:
+    """A decode step of an n-layer schedule on this cache: layer 0 Full with a
+    pool of 8192, then per run of 4 layers one Reindex layer (Top-K' 2048 of
+    the pool) and three Reuse layers of it; every layer with its own queries,
+    the indexer layers with their own indexer queries.  Layers run in order
+    (a layer's queries come from the previous layer's output)."""
+    from fp4_compressed_sparse_csa2_amd.schedule import Runner, Schedule
+    torch, gen = S.torch, S.gen
+    wl, dev, R = S.wl, S.dev, len(S.caches)
+    sched = Schedule.pattern(n_layers, 8192, 2048, period=4)
+    runners = [Runner(sched, S.caches[r]) for r in range(R)]
+    q_idx = {i: S.t(gen.idx_query(wl, i)) for i in sched.selecting_layers()}
+    q = [S.t(gen.query(wl, i)) for i in range(n_layers)]
+    outs = [torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    lses = [torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev) for _ in range(n_layers)]
+
+    def step(r):
+        runners[r].step(S.ctx, S.max_ctx, q_idx, q, [S.rings[r]] * n_layers, S.sigma, outs, lses)
+
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    t = time_call(S, step, R, reps=5)
+    modes = [l.mode for l in sched.layers]
+    return {"schedule": f"{n_layers} layers: " + ", ".join(f"{modes.count(m)} {m}" for m in
+                                                             ("full", "reindex", "reuse")),
+            "step_us": t, "us_per_layer": t / n_layers,
+            "layer_queries_per_s": wl.B * n_layers / (t * 1e-6)}
+
+
 # ------------------------------------------------------------------ sharded context
 def shard_bounds(L: int, n: int) -> list:
     """n page-aligned ascending position ranges covering [0, L); the last is open."""
@@ -647,6 +677,7 @@ def main() -> int:
     wl = S.wl
     wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
     chain = chain_calls(S)
+    chain["schedule"] = schedule_calls(S)
     copy_rate = copy_gbs(torch)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
