@@ -386,7 +386,8 @@ def gpu_bench(args, S: Setup):
     seq = torch.arange(B, dtype=torch.int32, device=S.dev).repeat_interleave(W)
     pos = torch.cat([torch.arange(int(L) - W, int(L), dtype=torch.int32, device=S.dev)
                      for L in S.lens])
-    tok = torch.stack([S.rings[0][b][pos[b * W:(b + 1) * W] % W] for b in range(B)]).reshape(B * W, -1)
+    tok = S.t(np.concatenate([S.ring_host[b][np.arange(int(L) - W, int(L)) % W]
+                              for b, L in enumerate(S.lens)]))
     restore_us = time_call(S, lambda r: S.csa2.quantize_append(S.caches[r], tok, seq, pos,
                                                                swa=S.rings[r]), R)
     spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
