@@ -105,3 +105,45 @@ def merge_topk(parts, K: int) -> tuple[np.ndarray, int]:
     order = rank_order(sc, pos)
     return _emit(pos[order[:min(K, pos.size)]], K)
 
+
+# ---------------------------------------------------------------- key scales
+# Indexer keys with a scale per token (the pages name the indexer "K / scale"
+# but give no formula).  Reading: each cached position p carries an fp32
+# scale s_p; the ranked value is v_p = fl32(s_p * score_p), the product
+# rounded once to float32 (round to nearest, ties to even); ranking is by v
+# descending, then position ascending, with -0 and +0 equal (a tie); scales
+# must be finite.  The integer score is exact in float32 (|score| <= 2^21).
+
+def scaled_values(scores: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """v = fl32(s * score) for int scores and float32 scales; -0 becomes +0."""
+    v = np.asarray(scales, dtype=np.float32) * np.asarray(scores, dtype=np.int64).astype(np.float32)
+    v = v.astype(np.float32)
+    v[v == 0] = np.float32(0.0)
+    return v
+
+
+def rank_order_values(values: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Permutation sorting entries by (value descending, position ascending)."""
+    v = np.asarray(values, dtype=np.float64)          # exact widening of float32
+    return np.lexsort((np.asarray(pos), -v))
+
+
+def topk_values(values: np.ndarray, L: int, K: int) -> tuple[np.ndarray, int, np.ndarray]:
+    """Full-layer selection ranked by float values over candidates [0, L-128):
+    (positions ascending, -1 padded to K; count; their values, 0 past it)."""
+    n = max(0, L - WINDOW)
+    pos = np.arange(n)
+    order = rank_order_values(values[:n], pos)
+    idx, c = _emit(pos[order[:min(K, n)]], K)
+    vals = np.zeros(K, dtype=np.float32)
+    vals[:c] = np.asarray(values, dtype=np.float32)[idx[:c]]
+    return idx, c, vals
+
+
+def reindex_values(pool: np.ndarray, pool_count: int, values_of_pool: np.ndarray,
+                   K: int) -> tuple[np.ndarray, int]:
+    """Reindex layer ranked by float values of the pool entries."""
+    p = np.asarray(pool[:pool_count], dtype=np.int64)
+    order = rank_order_values(values_of_pool[:pool_count], p)
+    return _emit(p[order[:min(K, pool_count)]], K)
+
