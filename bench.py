@@ -301,6 +301,68 @@ def chain_calls(S: Setup) -> dict:
             "reindex_gbs": rbytes / (t["reindex_8192_to_2048"] * 1e-6) / 1e9}
 
 
+def scaled_calls(S: Setup) -> dict:
+    """The scaled indexer (a fp32 key scale per token, ranked by
+    fl32(s * score)) at the step's shape: the Full layer's Top-K 2048 and a
+    Reindex 8192 -> 2048 over a scaled pool, with sequence 0 of the Full
+    layer checked against the oracle."""
+    from oracle import select as OS
+
+    torch, csa2, gen = S.torch, S.csa2, S.gen
+    wl, dev, R = S.wl, S.dev, len(S.caches)
+    B, K, Kf = wl.B, wl.K, gen.WORKLOADS["chain_64k"].K
+    host = [gen.key_scales(wl, b, int(S.lens[b])) for b in range(B)]
+    ks = [csa2.key_scales_for(c) for c in S.caches]
+    for b in range(B):
+        Lb = int(S.lens[b])
+        sb, pb = torch.full((Lb,), b, dtype=torch.int32, device=dev), \
+            torch.arange(Lb, dtype=torch.int32, device=dev)
+        for r in range(R):
+            csa2.store_key_scales(S.caches[r], S.t(host[b]), sb, pb, ks[r])
+    idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    pool = torch.empty((B, Kf), dtype=torch.int32, device=dev)
+    pc = torch.empty((B,), dtype=torch.int32, device=dev)
+    q1 = S.t(gen.idx_query(gen.WORKLOADS["chain_64k"], 1))
+    ws = [csa2.Workspace(dev) for _ in range(3)]
+
+    def topk(r):
+        csa2.index_topk_scaled(S.caches[r], S.ctx, S.max_ctx, S.q_idx, ks[r], K, ws[0],
+                               out_idx=idx, out_count=cnt)
+
+    def full_pool(r):
+        csa2.index_topk_scaled(S.caches[r], S.ctx, S.max_ctx, S.q_idx, ks[r], Kf, ws[1],
+                               out_idx=pool, out_count=pc)
+
+    def reindex(r):
+        csa2.reindex_scaled(S.caches[r], q1, ks[r], pool, pc, K, ws[2], out_idx=idx,
+                            out_count=cnt)
+
+    topk(0)
+    torch.cuda.synchronize()
+    L0 = int(S.lens[0])
+    v = OS.scaled_values(OS.indexer_scores(S.q_idx_h[0], S.keys[0][:L0 - 128]), host[0][:L0 - 128])
+    want, wc, _ = OS.topk_values(v, L0, K)
+    ok = int(cnt[0]) == wc and np.array_equal(idx[0].cpu().numpy(), want)
+    assert ok, "scaled Top-K differs from the oracle, b=0"
+    full_pool(0)
+    reindex(0)
+    torch.cuda.synchronize()
+    t_topk = time_call(S, topk, R)
+    t_full = time_call(S, full_pool, R)
+    full_pool(0)
+    torch.cuda.synchronize()
+    t_re = time_call(S, reindex, R)
+    L = int(S.lens.max())
+    nbytes = algorithmic_bytes(B, L, wl.H, wl.D, wl.Di, K)["index_topk"] + B * 4 * (L - 128)
+    return {"key_scales": "fp32 per token, exp(N(0,1))/128",
+            "parity": "sequence 0: Top-K bit-exact",
+            "calls_us": {"index_topk_scaled_2048": t_topk, "index_topk_scaled_8192": t_full,
+                         "reindex_scaled_8192_to_2048": t_re},
+            "index_topk_scaled_bytes": nbytes,
+            "index_topk_scaled_gbs": nbytes / (t_topk * 1e-6) / 1e9}
+
+
 def parity_check(S: Setup) -> str:
     """Sequences 0 and B-1 of the eager result against the oracle: indices
     bit-exact, outputs and LSE within 2e-3."""
@@ -679,6 +741,7 @@ def main() -> int:
     wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
     chain = chain_calls(S)
     chain["schedule"] = schedule_calls(S)
+    scaled = scaled_calls(S)
     copy_rate = copy_gbs(torch)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
@@ -722,6 +785,7 @@ def main() -> int:
                                "frac": dec_tflops / MFMA_F16_PEAK_TFLOPS},
         "copy_reference_gbs": copy_rate,
         "chain": chain,
+        "scaled_indexer": scaled,
         "roofline": {"kernel": "csa2_index_topk (" + ", ".join(STEP_KERNELS["index_topk"]) + ")",
                      "bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": topk_gbs / HBM_PEAK_GBS, "traffic": traffic,

@@ -13,13 +13,17 @@ from ._lib import (  # noqa: F401
     Workspace,
     index_topk,
     index_topk_range,
+    index_topk_scaled,
+    key_scales_for,
     lib,
     lse_merge,
     page_bytes,
     quantize_append,
     reindex,
+    reindex_scaled,
     restore_window,
     sparse_decode,
+    store_key_scales,
     topk_merge,
     workspace_init,
 )

@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
                                                _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_lse_merge": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                               _c_vp, _c_vp]),
+            "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+            "csa2_index_topk_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
+                                                      _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                                      _c_vp]),
+            "csa2_reindex_scaled": (ctypes.c_int, [P, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
+                                                   _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -284,6 +290,96 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
                                     _ptr(lse), w.data_ptr(), w.numel(), _stream(dev)),
            "csa2_sparse_decode")
     return out, lse
+
+
+# ------------------------------------------------------------------ key scales
+def key_scales_for(cache: Cache) -> torch.Tensor:
+    """A zeroed per-token key-scale array (float32 [num_pages, 64]) for cache."""
+    return torch.zeros((cache.pages.shape[0], PAGE_TOKENS), dtype=torch.float32,
+                       device=cache.device)
+
+
+def store_key_scales(cache: Cache, scale: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                     key_scales: torch.Tensor) -> None:
+    """Write the fp32 key scales of tokens at (seq, pos) into key_scales
+    [num_pages, 64] through the page table."""
+    dev = cache.device
+    n = scale.shape[0]
+    _need(scale, "scale", torch.float32, dev, (n,))
+    _need(seq, "seq", torch.int32, dev, (n,))
+    _need(pos, "pos", torch.int32, dev, (n,))
+    _need(key_scales, "key_scales", torch.float32, dev, (cache.pages.shape[0], PAGE_TOKENS))
+    _check(lib().csa2_store_key_scales(ctypes.byref(cache.struct), n, scale.data_ptr(),
+                                       seq.data_ptr(), pos.data_ptr(), key_scales.data_ptr(),
+                                       _stream(dev)),
+           "csa2_store_key_scales")
+
+
+def index_topk_scaled(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
+                      key_scales: torch.Tensor, K: int, ws: Workspace,
+                      out_idx: torch.Tensor | None = None, out_count: torch.Tensor | None = None,
+                      out_values: torch.Tensor | None = None,
+                      out_sel_values: torch.Tensor | None = None):
+    """Full layer ranked by v_p = fl32(s_p * score_p).  Returns (idx [B, K],
+    count [B], values of the selected [B, K] or None)."""
+    dev, B = cache.device, cache.batch
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    _need(key_scales, "key_scales", torch.float32, dev, (cache.pages.shape[0], PAGE_TOKENS))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    if out_values is not None:
+        _need(out_values, "out_values", torch.float32, dev, (B, max_ctx))
+    if out_sel_values is not None:
+        _need(out_sel_values, "out_sel_values", torch.float32, dev, (B, K))
+    nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
+    if nbytes == 0:
+        raise Csa2Error(f"index_topk_scaled: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_index_topk_scaled(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
+                                        q_idx.data_ptr(), key_scales.data_ptr(), K,
+                                        out_idx.data_ptr(), out_count.data_ptr(),
+                                        _ptr(out_values), _ptr(out_sel_values), w.data_ptr(),
+                                        w.numel(), _stream(dev)),
+           "csa2_index_topk_scaled")
+    return out_idx, out_count, out_sel_values
+
+
+def reindex_scaled(cache: Cache, q_idx: torch.Tensor, key_scales: torch.Tensor,
+                   pool: torch.Tensor, pool_count: torch.Tensor, K: int, ws: Workspace,
+                   out_idx: torch.Tensor | None = None, out_count: torch.Tensor | None = None,
+                   out_values: torch.Tensor | None = None):
+    """Reindex layer ranked by the scaled values of the pool [B, P] entries.
+    Returns (idx [B, K], count [B])."""
+    dev, B = cache.device, cache.batch
+    P = pool.shape[1]
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    _need(key_scales, "key_scales", torch.float32, dev, (cache.pages.shape[0], PAGE_TOKENS))
+    _need(pool, "pool", torch.int32, dev, (B, P))
+    _need(pool_count, "pool_count", torch.int32, dev, (B,))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    if out_values is not None:
+        _need(out_values, "out_values", torch.float32, dev, (B, P))
+    nbytes = lib().csa2_reindex_workspace_size(B, P, K)
+    if nbytes == 0:
+        raise Csa2Error(f"reindex_scaled: unsupported sizes B={B} P={P} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_reindex_scaled(ctypes.byref(cache.struct), q_idx.data_ptr(),
+                                     key_scales.data_ptr(), pool.data_ptr(),
+                                     pool_count.data_ptr(), P, K, out_idx.data_ptr(),
+                                     out_count.data_ptr(), _ptr(out_values), w.data_ptr(),
+                                     w.numel(), _stream(dev)),
+           "csa2_reindex_scaled")
+    return out_idx, out_count
 
 
 # ------------------------------------------------------------------ sharding

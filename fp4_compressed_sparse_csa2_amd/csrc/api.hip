@@ -106,8 +106,40 @@ int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max
   if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
   const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
   if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
-  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, 0, kMaxCtx,
-                                        out_idx, out_count, out_scores, nullptr, ws,
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, nullptr, K, 0,
+                                        kMaxCtx, out_idx, out_count, out_scores, nullptr, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float* scale,
+                          const int32_t* seq, const int32_t* pos, float* key_scales,
+                          void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (n_tokens < 0) return CSA2_E_SHAPE;
+  if (n_tokens > 0 && (scale == nullptr || seq == nullptr || pos == nullptr ||
+                       key_scales == nullptr))
+    return CSA2_E_NULL;
+  return status_of(csa2::run_store_key_scales(args_of(cache), n_tokens, scale, seq, pos,
+                                              key_scales, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_topk_scaled(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                           const int8_t* q_idx, const float* key_scales, int32_t K,
+                           int32_t* out_idx, int32_t* out_count, float* out_values,
+                           float* out_sel_values, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q_idx == nullptr || key_scales == nullptr || out_count == nullptr)
+    return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
+  const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, key_scales, K,
+                                        0, kMaxCtx, out_idx, out_count,
+                                        reinterpret_cast<int32_t*>(out_values),
+                                        reinterpret_cast<int32_t*>(out_sel_values), ws,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -123,9 +155,9 @@ int csa2_index_topk_range(const csa2_cache* cache, const int32_t* ctx_len, int32
   if (p_begin < 0 || p_begin % CSA2_PAGE_TOKENS != 0 || p_end < p_begin) return CSA2_E_SHAPE;
   const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
   if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
-  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, K, p_begin,
-                                        p_end, out_idx, out_count, nullptr, out_sel_scores, ws,
-                                        static_cast<hipStream_t>(stream)));
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, nullptr, K,
+                                        p_begin, p_end, out_idx, out_count, nullptr,
+                                        out_sel_scores, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa2_topk_merge_workspace_size(int32_t batch, int32_t n_parts, int32_t K_in, int32_t K) {
@@ -177,9 +209,26 @@ int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx, const int32_t* po
   if (P < 0 || P > kMaxK || K < 0 || K > P) return CSA2_E_SHAPE;
   const size_t need = csa2::reindex_ws_bytes(cache->batch, P, K);
   if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
-  return status_of(csa2::run_reindex(args_of(cache), q_idx, pool, pool_count, P, K, out_idx,
-                                     out_count, out_scores, ws,
+  return status_of(csa2::run_reindex(args_of(cache), q_idx, nullptr, pool, pool_count, P, K,
+                                     out_idx, out_count, out_scores, ws,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const float* key_scales,
+                        const int32_t* pool, const int32_t* pool_count, int32_t P, int32_t K,
+                        int32_t* out_idx, int32_t* out_count, float* out_values, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (q_idx == nullptr || key_scales == nullptr || pool_count == nullptr || out_count == nullptr)
+    return CSA2_E_NULL;
+  if ((P > 0 && pool == nullptr) || (K > 0 && out_idx == nullptr)) return CSA2_E_NULL;
+  if (P < 0 || P > kMaxK || K < 0 || K > P) return CSA2_E_SHAPE;
+  const size_t need = csa2::reindex_ws_bytes(cache->batch, P, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_reindex(args_of(cache), q_idx, key_scales, pool, pool_count, P, K,
+                                     out_idx, out_count, reinterpret_cast<int32_t*>(out_values),
+                                     ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa2_sparse_decode_workspace_size(int32_t batch, int32_t H, int32_t head_dim, int32_t K) {

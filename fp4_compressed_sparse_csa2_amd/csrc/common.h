@@ -32,6 +32,26 @@ __device__ __forceinline__ uint32_t score_key(int s) {
   return k > 0x3FFFFFu ? 0x3FFFFFu : k;
 }
 
+// Scaled indexer value of one position: fl32(s * score), the product rounded
+// once to float32 (round to nearest even).  An int8 score at Di <= 128 is
+// exact in float32 (|score| <= 2^21), so the conversion adds no rounding.
+// -0 becomes +0, so that the two zeros are one value (a tie).
+__device__ __forceinline__ float scaled_value(int score, float s) {
+  const float v = __fmul_rn((float)score, s);
+  return v == 0.0f ? 0.0f : v;
+}
+
+// Order key of a float32 value: keys compare (unsigned) as the values do,
+// -inf below every finite value below +inf.  Negative values flip every bit,
+// the others set the sign bit.  The caller passes +0 for a zero.
+__device__ __forceinline__ uint32_t value_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ lanes

@@ -10,6 +10,11 @@
 // and writes int32 scores plus a histogram of the top 11 bits of the biased
 // 22-bit key into the sequence's global histogram.  The selection kernels in
 // select.hip then take the deterministic Top-K.
+//
+// Scaled variant: each position also carries an fp32 key scale s_p (the
+// pages pair the indexer keys with a scale), stored [page][row] beside the
+// cache; the ranked value is fl32(s_p * score_p), kept as a 32-bit order key
+// whose top 11 bits feed the same histogram.
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -41,11 +46,12 @@ __device__ __forceinline__ int seq_candidates(const int32_t* ctx_len, int b, int
 }
 
 // ------------------------------------------------------------------ score
-template <int DI>
+template <int DI, bool SCALED>
 __global__ __launch_bounds__(kBlock) void index_score_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
     int max_pages, int keys_off, int page_bytes, const int32_t* __restrict__ ctx_len,
-    int max_ctx, int p_begin, int p_end, const int8_t* __restrict__ q_idx, int K,
+    int max_ctx, int p_begin, int p_end, const int8_t* __restrict__ q_idx,
+    const float* __restrict__ key_scales, int K,
     int32_t* __restrict__ scores, int32_t* __restrict__ out_scores, uint32_t* __restrict__ ctrl) {
   constexpr int LPP = DI / 16;        // lanes per position (16 key bytes each)
   constexpr int PPL = 64 / LPP;       // positions per 1 KB wave load
@@ -80,6 +86,7 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
   // waits only for its own loads.  The keys are read once per call:
   // non-temporal loads keep them from evicting what the next kernels reuse.
   uint4 v[kPagesPerWave][LPP];
+  float ks[kPagesPerWave];               // scaled: the key scale of page row ppos
   bool live[kPagesPerWave];
 #pragma unroll
   for (int pi = 0; pi < kPagesPerWave; ++pi) {
@@ -91,6 +98,9 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
       const u32x4 t = __builtin_nontemporal_load(kp + j * 64 + lane);
       v[pi][j] = make_uint4(t.x, t.y, t.z, t.w);
     }
+    if constexpr (SCALED)
+      ks[pi] = __builtin_nontemporal_load(key_scales + (size_t)(live[pi] ? pg[pi] : 0) * kPage +
+                                          ppos);
     __builtin_amdgcn_sched_barrier(0);   // keep the pages' loads in page order
   }
   if (do_hist) {                         // while the keys are on their way
@@ -112,9 +122,17 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
     }
     const int p = (lp0 + pi) * kPage + ppos;
     if (p < n) {
-      sc_row[p] = keep;
-      if (user_row) user_row[p_begin + p] = keep;
-      if (do_hist) atomicAdd(&hist[score_key(keep) >> 11], 1u);
+      if constexpr (SCALED) {
+        const float val = scaled_value(keep, ks[pi]);
+        const uint32_t key = value_key(val);
+        sc_row[p] = (int32_t)key;
+        if (user_row) user_row[p_begin + p] = (int32_t)__float_as_uint(val);
+        if (do_hist) atomicAdd(&hist[key >> FloatKeys::kTopShift], 1u);
+      } else {
+        sc_row[p] = keep;
+        if (user_row) user_row[p_begin + p] = keep;
+        if (do_hist) atomicAdd(&hist[score_key(keep) >> 11], 1u);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // pages in arrival order
   }
@@ -151,10 +169,21 @@ size_t index_topk_ws_bytes(int batch, int max_ctx, int /*K*/) {
   return topk_ws(batch, max_ctx).total;
 }
 
+template <int DI, bool SCALED>
+static void launch_score(const dim3& grid, hipStream_t st, const CacheArgs& c,
+                         const PageLayout& lay, const int32_t* ctx_len, int max_ctx, int p_begin,
+                         int p_end, const int8_t* q_idx, const float* key_scales, int K,
+                         int32_t* scores, int32_t* out_scores, uint32_t* ctrl) {
+  hipLaunchKernelGGL((index_score_kernel<DI, SCALED>), grid, dim3(kBlock), 0, st,
+                     (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
+                     lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx,
+                     key_scales, K, scores, out_scores, ctrl);
+}
+
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
-                          const int8_t* q_idx, int K, int p_begin, int p_end, int32_t* out_idx,
-                          int32_t* out_count, int32_t* out_scores, int32_t* out_sel_scores,
-                          void* ws, hipStream_t st) {
+                          const int8_t* q_idx, const float* key_scales, int K, int p_begin,
+                          int p_end, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                          int32_t* out_sel_scores, void* ws, hipStream_t st) {
   const TopkWs w = topk_ws(c.batch, max_ctx);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + w.ctrl);
@@ -165,16 +194,19 @@ hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ct
   const int max_entries = hi > p_begin ? hi - p_begin : 0;
   const int n_chunks = (max_entries + kChunk - 1) / kChunk;
   const dim3 grid(n_chunks > 0 ? n_chunks : 1, c.batch);
-  if (c.Di == 128)
-    hipLaunchKernelGGL(index_score_kernel<128>, grid, dim3(kBlock), 0, st,
-                       (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx, K,
-                       scores, out_scores, ctrl);
+  const bool scaled = key_scales != nullptr;
+  if (c.Di == 128 && !scaled)
+    launch_score<128, false>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx, nullptr,
+                             K, scores, out_scores, ctrl);
+  else if (c.Di == 128)
+    launch_score<128, true>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx,
+                            key_scales, K, scores, out_scores, ctrl);
+  else if (!scaled)
+    launch_score<64, false>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx, nullptr,
+                            K, scores, out_scores, ctrl);
   else
-    hipLaunchKernelGGL(index_score_kernel<64>, grid, dim3(kBlock), 0, st,
-                       (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                       lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx, K,
-                       scores, out_scores, ctrl);
+    launch_score<64, true>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx,
+                           key_scales, K, scores, out_scores, ctrl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelectArgs a;
@@ -196,6 +228,7 @@ hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ct
   a.out_idx = out_idx;
   a.out_count = out_count;
   a.out_sel_scores = out_sel_scores;
+  a.float_keys = scaled ? 1 : 0;
   return run_select(a, max_entries, st);
 }
 

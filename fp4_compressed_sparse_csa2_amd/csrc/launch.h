@@ -19,7 +19,8 @@ struct CacheArgs {
 
 hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st);
 
-// One selection call over per-sequence int32 scores (see select.hip).  The
+// One selection call over per-sequence int32 scores, or float order keys
+// (float_keys != 0; see select.hip).  The
 // entries of sequence b are 0 <= i < n_b with n_b from ctx_len (candidates
 // of a Full layer, i = position) or from pool_count (a Reindex layer's pool,
 // output id = pool[b][i]).
@@ -41,7 +42,8 @@ struct SelectArgs {
   uint32_t* chunk_counts;     // [batch][kMaxSelChunks]
   int32_t* out_idx;           // [batch][K]
   int32_t* out_count;         // [batch]
-  int32_t* out_sel_scores;    // [batch][K] scores of the selected entries, or NULL
+  int32_t* out_sel_scores;    // [batch][K] scores (float bits for float keys), or NULL
+  int float_keys;             // 0: scores are int32 indexer scores; 1: value_key words
 };
 hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st);
 
@@ -49,16 +51,24 @@ hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, con
                                const int32_t* seq, const int32_t* pos, uint16_t* swa,
                                hipStream_t st);
 
+// key_scales: NULL for int32 scores, else float [num_pages][64] per-token
+// scales; the ranked values are then scaled_value(score, scale) and the
+// score outputs carry float bits.
 size_t index_topk_ws_bytes(int batch, int max_ctx, int K);
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
-                          const int8_t* q_idx, int K, int p_begin, int p_end, int32_t* out_idx,
-                          int32_t* out_count, int32_t* out_scores, int32_t* out_sel_scores,
-                          void* ws, hipStream_t st);
+                          const int8_t* q_idx, const float* key_scales, int K, int p_begin,
+                          int p_end, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                          int32_t* out_sel_scores, void* ws, hipStream_t st);
 
 size_t reindex_ws_bytes(int batch, int P, int K);
-hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* pool,
-                       const int32_t* pool_count, int P, int K, int32_t* out_idx,
-                       int32_t* out_count, int32_t* out_scores, void* ws, hipStream_t st);
+hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const float* key_scales,
+                       const int32_t* pool, const int32_t* pool_count, int P, int K,
+                       int32_t* out_idx, int32_t* out_count, int32_t* out_scores, void* ws,
+                       hipStream_t st);
+
+hipError_t run_store_key_scales(const CacheArgs& c, int n, const float* scale,
+                                const int32_t* seq, const int32_t* pos, float* key_scales,
+                                hipStream_t st);
 
 size_t topk_merge_ws_bytes(int batch, int n_parts, int K_in, int K);
 hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,

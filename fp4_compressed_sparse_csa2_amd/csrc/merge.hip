@@ -120,6 +120,7 @@ hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
   a.out_idx = out_idx;
   a.out_count = out_count;
   a.out_sel_scores = out_sel_scores;
+  a.float_keys = 0;
   return run_select(a, P, st);
 }
 

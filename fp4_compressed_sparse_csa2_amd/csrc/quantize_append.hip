@@ -90,4 +90,30 @@ hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, con
   return hipErrorInvalidValue;
 }
 
+// Key scales of appended tokens: scale[i] goes to key_scales[pg][p % 64] for
+// token i at (seq[i], pos[i]) with pg its page; tokens that do not map to a
+// page are skipped, as in the append above.
+__global__ __launch_bounds__(kBlock) void store_key_scales_kernel(
+    const int32_t* __restrict__ page_table, int num_pages, int max_pages, int batch, int n,
+    const float* __restrict__ scale, const int32_t* __restrict__ seq,
+    const int32_t* __restrict__ pos, float* __restrict__ key_scales) {
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const int b = seq[i], p = pos[i];
+  if (b < 0 || b >= batch || p < 0 || p >= max_pages * kPage) return;
+  const int pg = page_table[(size_t)b * max_pages + p / kPage];
+  if (pg < 0 || pg >= num_pages) return;
+  key_scales[(size_t)pg * kPage + p % kPage] = scale[i];
+}
+
+hipError_t run_store_key_scales(const CacheArgs& c, int n, const float* scale,
+                                const int32_t* seq, const int32_t* pos, float* key_scales,
+                                hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(store_key_scales_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0,
+                     st, c.page_table, c.num_pages, c.max_pages, c.batch, n, scale, seq, pos,
+                     key_scales);
+  return hipGetLastError();
+}
+
 }  // namespace csa2

@@ -12,7 +12,8 @@
 // entry's 64 or 128 key bytes read by 4 or 8 lanes), scores them with v_dot4
 // and histograms the top digit; the selection kernels of select.hip then
 // take Top-K' over the pool entries, which are in ascending position order,
-// and map the winners back to positions.
+// and map the winners back to positions.  The scaled variant ranks the
+// float32 values fl32(s_p * score_p) with the per-token key scales instead.
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -21,10 +22,11 @@ namespace csa2 {
 
 constexpr int kREntries = 256;          // pool entries per block
 
-template <int DI>
+template <int DI, bool SCALED>
 __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
     const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
     int max_pages, int keys_off, int page_bytes, const int8_t* __restrict__ q_idx,
+    const float* __restrict__ key_scales,
     const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_count, int P, int K,
     int32_t* __restrict__ scores, int stride, int32_t* __restrict__ out_scores,
     uint32_t* __restrict__ ctrl) {
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
   const int wbase = e0 + wave * 64;
   uint4 v[LPP];
   bool ok[LPP];
+  int srow = -1;                        // scaled: key-scale slot of the entry this lane keeps
 #pragma unroll
   for (int j = 0; j < LPP; ++j) {       // entry wbase + j*PPL + lane/LPP
     const int e = wbase + j * PPL + lane / LPP;
@@ -61,7 +64,10 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
     if (ok[j])
       v[j] = *reinterpret_cast<const uint4*>(pages + (size_t)pg * page_bytes + keys_off +
                                              (p % kPage) * DI + (lane % LPP) * 16);
+    if (SCALED && (lane % LPP) == j && ok[j]) srow = pg * kPage + p % kPage;
   }
+  float ks = 0.0f;
+  if constexpr (SCALED) ks = srow >= 0 ? key_scales[srow] : 0.0f;
   int keep = 0;
   bool keep_ok = false;
 #pragma unroll
@@ -81,11 +87,20 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
   }
   const int e = wbase + PPL * (lane % LPP) + lane / LPP;
   if (e < c) {
-    // an unusable entry (contract violation) ranks below every real score
-    const int s = keep_ok ? keep : -kKeyBias;
-    sc_row[e] = s;
-    if (out_scores != nullptr) out_scores[(size_t)b * P + e] = s;
-    if (do_hist) atomicAdd(&hist[score_key(s) >> 11], 1u);
+    if constexpr (SCALED) {
+      // an unusable entry ranks as -inf, below every finite value
+      const float val = keep_ok ? scaled_value(keep, ks) : -__builtin_inff();
+      const uint32_t key = value_key(val);
+      sc_row[e] = (int32_t)key;
+      if (out_scores != nullptr) out_scores[(size_t)b * P + e] = (int32_t)__float_as_uint(val);
+      if (do_hist) atomicAdd(&hist[key >> FloatKeys::kTopShift], 1u);
+    } else {
+      // an unusable entry (contract violation) ranks below every real score
+      const int s = keep_ok ? keep : -kKeyBias;
+      sc_row[e] = s;
+      if (out_scores != nullptr) out_scores[(size_t)b * P + e] = s;
+      if (do_hist) atomicAdd(&hist[score_key(s) >> 11], 1u);
+    }
   }
   if (do_hist) {
     __syncthreads();
@@ -115,9 +130,21 @@ static ReindexWs reindex_ws(int batch, int P) {
 
 size_t reindex_ws_bytes(int batch, int P, int /*K*/) { return reindex_ws(batch, P).total; }
 
-hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* pool,
-                       const int32_t* pool_count, int P, int K, int32_t* out_idx,
-                       int32_t* out_count, int32_t* out_scores, void* ws, hipStream_t st) {
+template <int DI, bool SCALED>
+static void launch_rescore(const dim3& grid, hipStream_t st, const CacheArgs& c,
+                           const PageLayout& lay, const int8_t* q_idx, const float* key_scales,
+                           const int32_t* pool, const int32_t* pool_count, int P, int K,
+                           int32_t* scores, int stride, int32_t* out_scores, uint32_t* ctrl) {
+  hipLaunchKernelGGL((reindex_score_kernel<DI, SCALED>), grid, dim3(kBlock), 0, st,
+                     (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
+                     lay.keys_off, lay.page_bytes, q_idx, key_scales, pool, pool_count, P, K,
+                     scores, stride, out_scores, ctrl);
+}
+
+hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const float* key_scales,
+                       const int32_t* pool, const int32_t* pool_count, int P, int K,
+                       int32_t* out_idx, int32_t* out_count, int32_t* out_scores, void* ws,
+                       hipStream_t st) {
   const ReindexWs w = reindex_ws(c.batch, P);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + w.ctrl);
@@ -126,16 +153,18 @@ hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* p
   const PageLayout lay = page_layout(c.D, c.Di);
   if (P > 0) {
     const dim3 grid((P + kREntries - 1) / kREntries, c.batch);
-    if (c.Di == 128)
-      hipLaunchKernelGGL(reindex_score_kernel<128>, grid, dim3(kBlock), 0, st,
-                         (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                         lay.keys_off, lay.page_bytes, q_idx, pool, pool_count, P, K, scores,
-                         stride, out_scores, ctrl);
+    if (c.Di == 128 && key_scales == nullptr)
+      launch_rescore<128, false>(grid, st, c, lay, q_idx, nullptr, pool, pool_count, P, K,
+                                 scores, stride, out_scores, ctrl);
+    else if (c.Di == 128)
+      launch_rescore<128, true>(grid, st, c, lay, q_idx, key_scales, pool, pool_count, P, K,
+                                scores, stride, out_scores, ctrl);
+    else if (key_scales == nullptr)
+      launch_rescore<64, false>(grid, st, c, lay, q_idx, nullptr, pool, pool_count, P, K,
+                                scores, stride, out_scores, ctrl);
     else
-      hipLaunchKernelGGL(reindex_score_kernel<64>, grid, dim3(kBlock), 0, st,
-                         (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                         lay.keys_off, lay.page_bytes, q_idx, pool, pool_count, P, K, scores,
-                         stride, out_scores, ctrl);
+      launch_rescore<64, true>(grid, st, c, lay, q_idx, key_scales, pool, pool_count, P, K,
+                               scores, stride, out_scores, ctrl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -158,6 +187,7 @@ hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const int32_t* p
   a.out_idx = out_idx;
   a.out_count = out_count;
   a.out_sel_scores = nullptr;
+  a.float_keys = key_scales != nullptr ? 1 : 0;
   return run_select(a, P, st);
 }
 

@@ -3,10 +3,12 @@
 //
 // Ranking is score descending, position ascending (ties go to the lower
 // position).  Scores are biased to 22-bit unsigned keys (score_key), so two
-// 11-bit digits fix the K-th largest key tau exactly; every key above tau is
-// selected, and of the keys equal to tau the ones with the lowest ids fill
-// the remaining slots.  Candidates are kept in ascending id order from the
-// start, so the emission is one stable compaction: no sort, no bitmap.
+// 11-bit digits fix the K-th largest key tau exactly (float32 values of a
+// scaled indexer take 32-bit order keys and a third, 10-bit digit); every
+// key above tau is selected, and of the keys equal to tau the ones with the
+// lowest ids fill the remaining slots.  Candidates are kept in ascending id
+// order from the start, so the emission is one stable compaction: no sort,
+// no bitmap.
 #pragma once
 
 #include "common.h"
@@ -149,6 +151,35 @@ __device__ void find_two_digits(const DigitBins<NT>& d1, const DigitBins<NT>& d2
 __device__ __forceinline__ int32_t key_score(uint32_t key) {
   return key == 0x3FFFFFu ? (1 << 21) : (int32_t)key - kKeyBias;
 }
+
+// How the 32-bit words of a score row map to radix keys.
+//   IntKeys   - int32 indexer scores; 22-bit biased keys (score_key), two
+//               11-bit digits.
+//   FloatKeys - the words are already order keys of float32 values
+//               (value_key); three digits of 11, 11 and 10 bits.
+// top(k) is the digit of the scoring kernels' histogram, mid(k) the digit of
+// the second histogram, low(k) the third digit (FloatKeys only).
+// out_word(k) is what a selection reports for the entry: the int32 score, or
+// the bits of the float32 value.
+struct IntKeys {
+  static constexpr bool kThree = false;
+  static constexpr int kTopShift = 11;
+  __device__ static uint32_t key(int32_t w) { return score_key(w); }
+  __device__ static uint32_t mid(uint32_t k) { return k & (kBins - 1); }
+  __device__ static uint32_t low(uint32_t) { return 0u; }
+  __device__ static int32_t out_word(uint32_t k) { return key_score(k); }
+  __device__ static int32_t stored_out(int32_t w) { return w; }
+};
+struct FloatKeys {
+  static constexpr bool kThree = true;
+  static constexpr int kTopShift = 21;
+  static constexpr int kLowBits = 10;
+  __device__ static uint32_t key(int32_t w) { return (uint32_t)w; }
+  __device__ static uint32_t mid(uint32_t k) { return (k >> kLowBits) & (kBins - 1); }
+  __device__ static uint32_t low(uint32_t k) { return k & ((1u << kLowBits) - 1u); }
+  __device__ static int32_t out_word(uint32_t k) { return (int32_t)__float_as_uint(key_value(k)); }
+  __device__ static int32_t stored_out(int32_t w) { return out_word((uint32_t)w); }
+};
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),

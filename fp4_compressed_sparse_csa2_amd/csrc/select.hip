@@ -62,19 +62,22 @@ __device__ __forceinline__ int32_t sel_id(const SelectArgs& a, int b, uint32_t i
 }
 
 // The j-th selected entry c = {key, entry} of sequence b: its id, and its
-// score when the caller asked for them.
+// score (or value) when the caller asked for them.
+template <typename KT>
 __device__ __forceinline__ void put_sel(const SelectArgs& a, int b, int j, uint2 c) {
   a.out_idx[(size_t)b * a.K + j] = sel_id(a, b, c.y);
-  if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = key_score(c.x);
+  if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = KT::out_word(c.x);
 }
 
 // K = 0 or every entry selected: the first min(K, n) entries in order, then -1.
+template <typename KT>
 __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, int nt) {
   int32_t* out = a.out_idx + (size_t)b * a.K;
   const int32_t* row = a.scores + (size_t)b * a.stride;
   for (int i = threadIdx.x; i < a.K; i += nt) {
     out[i] = i < n ? sel_id(a, b, (uint32_t)i) : -1;
-    if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + i] = i < n ? row[i] : 0;
+    if (a.out_sel_scores != nullptr)
+      a.out_sel_scores[(size_t)b * a.K + i] = i < n ? KT::stored_out(row[i]) : 0;
   }
   if (threadIdx.x == 0) a.out_count[b] = n < a.K ? n : a.K;
 }
@@ -85,19 +88,20 @@ __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, in
 // of a wave reads 1 KB of consecutive scores.  In entry order the kept
 // entries of a wave are ordered by (i, lane, k); a lane's place among them
 // comes from ballots of its per-load counts.
+template <typename KT>
 __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
   __shared__ uint2 list[kSingleListCap];
   __shared__ int scan_scratch[kSelWaves];
   __shared__ int round_tot[2][kSelWaves];
   __shared__ int2 wave_tot[kSelWaves];
-  __shared__ int sh_t1, sh_above1, sh_t2, sh_above2;
+  __shared__ int sh_t1, sh_above1, sh_t2, sh_above2, sh_t3, sh_above3;
 
   const int b = blockIdx.x;
   const int n = sel_entries(a, b);
   const int K = a.K;
   if (K == 0 || n <= K) {
-    select_all(a, b, n, kSelNT);
+    select_all<KT>(a, b, n, kSelNT);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -124,8 +128,14 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
   // digit >= t1  <=>  score >= lo (score_key folds only the top score, which
-  // is above every threshold a digit can set)
+  // is above every threshold a digit can set); for float keys, key >= lo_key
   const int lo = sh_t1 < 0 ? INT_MAX : (int)(t1 << 11) - kKeyBias;
+  const bool have_t1 = sh_t1 >= 0;
+  const uint32_t lo_key = t1 << KT::kTopShift;
+  auto kept = [&](int w) -> bool {
+    if constexpr (KT::kThree) return have_t1 && (uint32_t)w >= lo_key;
+    else return w >= lo;
+  };
 
   int total = 0;
   // kept-entry mask of load i (bit k: entry e0 + k) and its in-wave counts
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
     const int w[4] = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
     uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) m |= (w[k] >= lo && e0 + k < n) ? (1u << k) : 0u;
+    for (int k = 0; k < 4; ++k) m |= (kept(w[k]) && e0 + k < n) ? (1u << k) : 0u;
     return m;
   };
   auto keep_round = [&](const uint4 (&v)[kSelLd], int r) {
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if ((m >> k) & 1u) {
-            const uint2 cc = make_uint2(score_key(w[k]), (uint32_t)(e0 + k));
+            const uint2 cc = make_uint2(KT::key(w[k]), (uint32_t)(e0 + k));
             if (slot < kSingleListCap) list[slot] = cc; else ovf[slot] = cc;
             ++slot;
           }
@@ -188,20 +198,35 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   }
   __syncthreads();
   auto get = [&](int f) -> uint2 { return f < kSingleListCap ? list[f] : ovf[f]; };
-  // low-digit histogram of the kept entries whose top digit is t1
+  // second-digit histogram of the kept entries whose top digit is t1
   for (int f = tid; f < total; f += kSelNT) {
     const uint2 c = get(f);
-    if ((c.x >> 11) == t1) atomicAdd(&hist2[c.x & (kBins - 1)], 1u);
+    if ((c.x >> KT::kTopShift) == t1) atomicAdd(&hist2[KT::mid(c.x)], 1u);
   }
   __syncthreads();
 
   find_digit<kSelNT>(hist2, K - sh_above1, scan_scratch, &sh_t2, &sh_above2);
-  const uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
-  const int need_ties = K - sh_above1 - sh_above2;
+  uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
+  int need_ties = K - sh_above1 - sh_above2;
+  if constexpr (KT::kThree) {
+    // third digit: histogram (in hist2, whose bins every thread has read) of
+    // the kept entries whose top 22 bits are the threshold's
+    for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = sh_t2 >= 0 ? tau : 0xFFFFFFFFu;
+    for (int f = tid; f < total; f += kSelNT) {
+      const uint2 c = get(f);
+      if ((c.x >> KT::kLowBits) == pre) atomicAdd(&hist2[KT::low(c.x)], 1u);
+    }
+    __syncthreads();
+    find_digit<kSelNT>(hist2, need_ties, scan_scratch, &sh_t3, &sh_above3);
+    tau = sh_t3 >= 0 ? (pre << KT::kLowBits) | (uint32_t)sh_t3 : 0xFFFFFFFFu;
+    need_ties = sh_t3 >= 0 ? need_ties - sh_above3 : 0;
+  }
   int32_t* out = a.out_idx + (size_t)b * K;
   const int written = emit_in_order<kSelNT>(
       get, total, tau, need_ties, K, wave_tot,
-      [&](int j, uint2 c) { put_sel(a, b, j, c); });
+      [&](int j, uint2 c) { put_sel<KT>(a, b, j, c); });
   for (int j = written + tid; j < K; j += kSelNT) {
     out[j] = -1;
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
@@ -215,6 +240,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
 // at least t1 in entry order in the chunk's own slot list, counts them, and
 // adds the low digits of those whose top digit equals t1 to the sequence's
 // low-digit histogram.
+template <typename KT>
 __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
   __shared__ int scan_scratch[kBlock / 64];
   __shared__ int sh_t1, sh_above1;
@@ -245,9 +271,9 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
     const int w[4] = {(int)sv[i].x, (int)sv[i].y, (int)sv[i].z, (int)sv[i].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t kk = score_key(w[k]);
+      const uint32_t kk = KT::key(w[k]);
       key[4 * i + k] = kk;
-      keep |= (p0 + 4 * i + k < n && (kk >> 11) >= t1) ? 1u << (4 * i + k) : 0u;
+      keep |= (p0 + 4 * i + k < n && (kk >> KT::kTopShift) >= t1) ? 1u << (4 * i + k) : 0u;
     }
   }
   int chunk_total;
@@ -257,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
   for (int e = 0; e < kFiltPer; ++e) {
     if ((keep >> e) & 1u) {
       dst[slot++] = make_uint2(key[e], (uint32_t)(p0 + e));
-      if ((key[e] >> 11) == t1) atomicAdd(&ctrl[kCtrlHist2 + (key[e] & (kBins - 1))], 1u);
+      if ((key[e] >> KT::kTopShift) == t1) atomicAdd(&ctrl[kCtrlHist2 + KT::mid(key[e])], 1u);
     }
   }
   if (threadIdx.x == 0) a.chunk_counts[(size_t)b * kMaxSelChunks + chunk] = (uint32_t)chunk_total;
@@ -275,8 +301,10 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 // chunk's picks from registers after one barrier.  Otherwise the slot lists
 // are concatenated in LDS (the overflow read from the lists themselves) and
 // emitted in order.
-template <int SPL>
-
+// Float keys take a third digit from an LDS histogram of the candidates
+// whose top 22 bits are the threshold's, counted from registers (direct) or
+// from the concatenated list (general).
+template <int SPL, typename KT>
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   constexpr int spl = SPL;
   __shared__ int offs[kMaxSelChunks + 1];
@@ -284,16 +312,19 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   __shared__ unsigned long long scan64[kSelWaves];
   __shared__ int scan_scratch[kSelWaves];
   __shared__ int2 wave_tot[kSelWaves];
-  __shared__ int sh[4];
+  __shared__ int sh[6];
+  __shared__ uint32_t hist3[KT::kThree ? kBins : 1];
 
   const int b = blockIdx.x;
   const int n = sel_entries(a, b);
   const int K = a.K;
   if (K == 0 || n <= K) {
-    select_all(a, b, n, kSelNT);
+    select_all<KT>(a, b, n, kSelNT);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (KT::kThree)                      // visible after find_two_digits' barriers
+    for (int i = tid; i < kBins; i += kSelNT) hist3[i] = 0u;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   uint32_t* h2 = h1 + kCtrlHist2;
   const uint32_t* counts = a.chunk_counts + (size_t)b * kMaxSelChunks;
@@ -324,8 +355,24 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   // entries; if they do not (a workspace that was not zeroed), nothing is
   // selected
   const bool have_tau = sh[0] >= 0 && sh[2] >= 0;
-  const uint32_t tau = have_tau ? ((uint32_t)sh[0] << 11) | (uint32_t)sh[2] : 0xFFFFFFFFu;
-  const int need_ties = have_tau ? K - sh[1] - sh[3] : 0;
+  uint32_t tau = have_tau ? ((uint32_t)sh[0] << 11) | (uint32_t)sh[2] : 0xFFFFFFFFu;
+  int need_ties = have_tau ? K - sh[1] - sh[3] : 0;
+  // float keys: tau so far is the threshold's top 22 bits; count the third
+  // digit of the candidates that share them (count(f) visits each candidate
+  // once), then fix the full threshold.  All threads must call.
+  auto third_digit = [&](auto count) {
+    if constexpr (KT::kThree) {
+      const uint32_t pre = tau;
+      count([&](uint32_t key) {
+        if ((key >> KT::kLowBits) == pre) atomicAdd(&hist3[KT::low(key)], 1u);
+      });
+      __syncthreads();
+      find_digit<kSelNT>(hist3, have_tau ? need_ties : 1, scan_scratch, &sh[4], &sh[5]);
+      const bool ok = have_tau && sh[4] >= 0;
+      tau = ok ? (pre << KT::kLowBits) | (uint32_t)sh[4] : 0xFFFFFFFFu;
+      need_ties = ok ? need_ties - sh[5] : 0;
+    }
+  };
 
   int cmax = 0, off = 0;
   if (few) {
@@ -346,6 +393,11 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       e[2 * j] = make_uint2(sv[j].x, sv[j].y);
       e[2 * j + 1] = make_uint2(sv[j].z, sv[j].w);
     }
+    third_digit([&](auto add) {
+#pragma unroll
+      for (int k = 0; k < spl; ++k)
+        if (spl * lane + k < cnt) add(e[k].x);
+    });
     uint32_t gtm = 0, tiem = 0;
 #pragma unroll
     for (int k = 0; k < spl; ++k) {
@@ -379,10 +431,10 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     for (int k = 0; k < spl; ++k) {
       if ((gtm >> k) & 1u) {
         const int slot = g + (t < need_ties ? t : need_ties);
-        if (slot < K) put_sel(a, b, slot, e[k]);
+        if (slot < K) put_sel<KT>(a, b, slot, e[k]);
         ++g;
       } else if ((tiem >> k) & 1u) {
-        if (t < need_ties && g + t < K) put_sel(a, b, g + t, e[k]);
+        if (t < need_ties && g + t < K) put_sel<KT>(a, b, g + t, e[k]);
         ++t;
       }
     }
@@ -419,8 +471,11 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       }
       return cand_row[(size_t)lo * kFiltChunk + (f - offs[lo])];
     };
+    third_digit([&](auto add) {
+      for (int f = tid; f < total; f += kSelNT) add(get(f).x);
+    });
     written = emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot,
-                                    [&](int j, uint2 c) { put_sel(a, b, j, c); });
+                                    [&](int j, uint2 c) { put_sel<KT>(a, b, j, c); });
   }
   for (int j = written + tid; j < K; j += kSelNT) {
     out[j] = -1;
@@ -431,23 +486,29 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ host
-hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st) {
+template <typename KT>
+static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStream_t st) {
   if (max_entries <= kSingleMax) {
-    hipLaunchKernelGGL(select_single_kernel, dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL(select_single_kernel<KT>, dim3(a.batch), dim3(kSelNT), 0, st, a);
     return hipGetLastError();
   }
   const int chunks = (max_entries + kFiltChunk - 1) / kFiltChunk;
-  hipLaunchKernelGGL(select_filter_kernel, dim3(chunks, a.batch), dim3(kBlock), 0, st, a);
+  hipLaunchKernelGGL(select_filter_kernel<KT>, dim3(chunks, a.batch), dim3(kBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 16 candidates per lane in the direct plan when a chunk is expected to
   // keep more than ~400 (K's share of a chunk, with 25% to spare)
   const bool wide = (long long)a.K * kFiltChunk * 5 > (long long)max_entries * 4 * 8 * 64;
   if (wide)
-    hipLaunchKernelGGL(select_final_kernel<16>, dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<16, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   else
-    hipLaunchKernelGGL(select_final_kernel<8>, dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<8, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st) {
+  return a.float_keys ? run_select_keys<FloatKeys>(a, max_entries, st)
+                      : run_select_keys<IntKeys>(a, max_entries, st);
 }
 
 }  // namespace csa2

@@ -34,6 +34,7 @@ PAGE = 64             # KV rows per page
 
 # tensor ids for the sub-streams
 T_KV, T_KEYS, T_QIDX, T_Q, T_BOOST, T_LENS, T_PERM, T_APPEND_X, T_APPEND_K, T_SWA = range(10)
+T_KSCALE = 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -158,6 +159,33 @@ def idx_keys(wl: Workload, b: int, n: int) -> np.ndarray:
         kb = k[mask].astype(np.int32) + delta[None, :]
         k[mask] = np.clip(kb, -127, 127).astype(np.int8)
     return k
+
+
+def key_scales(wl: Workload, b: int, n: int, mode: str = "lognormal") -> np.ndarray:
+    """Per-token fp32 indexer-key scales of sequence b, float32 [n].
+
+    lognormal  exp(N(0, 1)) / 128: positive, spread over about two decades
+               (the magnitude of an absmax / 127 quantisation scale)
+    pow2       2^U{-3..3}: products of different scores collide exactly
+    fine       1 + U{0..1023} * 2^-23: equal scores give values that differ
+               only in their lowest mantissa bits
+    signed     lognormal with a random sign, and about 5% exact zeros
+    subnormal  lognormal times 2^-140: most products are float32 subnormals"""
+    r = _rng(wl, T_KSCALE, 0, b)
+    if mode == "pow2":
+        return np.ldexp(np.float32(1.0), r.integers(-3, 3, size=n, endpoint=True)).astype(np.float32)
+    if mode == "fine":
+        return (np.float32(1.0) + r.integers(0, 1023, size=n, endpoint=True).astype(np.float32)
+                * np.float32(2.0 ** -23)).astype(np.float32)
+    s = (np.exp(r.standard_normal(n)) / 128.0).astype(np.float32)
+    if mode == "signed":
+        s = np.where(r.random(n) < 0.5, -s, s).astype(np.float32)
+        s[r.random(n) < 0.05] = np.float32(0.0)
+    elif mode == "subnormal":
+        s = (s * np.float32(2.0 ** -140)).astype(np.float32)
+    elif mode != "lognormal":
+        raise ValueError(f"unknown key-scale mode {mode!r}")
+    return s
 
 
 def query(wl: Workload, layer: int = 0) -> np.ndarray:

@@ -304,6 +304,65 @@ int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t*
 int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
                    const float* outs, const float* lses, float* out, float* lse, void* stream);
 
+/*
+ * Indexer keys with a per-token scale.  The owner layer's state holds the
+ * indexer keys together with their scale (zulogic, "DeepSeek V4 1-Flash
+ * 架构拆解", section 3, the owner-layer state diagram); the page gives no
+ * formula, so the reading here is: every cached position p carries one fp32
+ * scale s_p, and the ranked value is
+ *   v_p = fl32(s_p * score_p)
+ * (the int32 score is exact in float32; one round-to-nearest-even rounding),
+ * with -0 taken as +0.  Order: value descending, position ascending; equal
+ * values (including the two zeros) are ties that go to the lower position.
+ * Scales must be finite; a non-finite scale gives an unspecified order for
+ * its sequence (never an out-of-bounds access).
+ *
+ * key_scales  device float [num_pages][64]: the scale of page row r of
+ *             physical page g at key_scales[64*g + r], beside the pages
+ *             (caller-owned, filled by csa2_store_key_scales).
+ */
+
+/*
+ * csa2_store_key_scales -- write the key scales of appended tokens.
+ * scale[i] goes to the row of position pos[i] of sequence seq[i] (its page
+ * from the page table); tokens whose (seq, pos) does not map to a page in
+ * [0, num_pages) are skipped, as in csa2_quantize_append.
+ * scale device float [n_tokens]; seq, pos device int32 [n_tokens].
+ * Errors: CSA2_E_NULL, CSA2_E_UNSUPPORTED, CSA2_E_SHAPE.
+ */
+int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float* scale,
+                          const int32_t* seq, const int32_t* pos, float* key_scales,
+                          void* stream);
+
+/*
+ * csa2_index_topk_scaled -- csa2_index_topk ranked by the scaled values v_p.
+ * out_idx / out_count as csa2_index_topk (the first min(K, n) candidates in
+ * (value descending, position ascending) order, ascending, -1 padded).
+ * out_values      device float [batch][max_ctx] or NULL: v_p of every
+ *                 candidate p < n (other entries untouched).
+ * out_sel_values  device float [batch][K] or NULL: v_p of each selected
+ *                 position (aligned with out_idx), 0 past the count.
+ * ws              workspace of csa2_index_topk_workspace_size(batch, max_ctx, K).
+ * Errors: as csa2_index_topk, and CSA2_E_NULL for key_scales.
+ */
+int csa2_index_topk_scaled(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,
+                           const int8_t* q_idx, const float* key_scales, int32_t K,
+                           int32_t* out_idx, int32_t* out_count, float* out_values,
+                           float* out_sel_values, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_reindex_scaled -- csa2_reindex ranked by the scaled values v_p of the
+ * pool entries (this layer's q_idx against the shared keys and scales).
+ * out_values  device float [batch][P] or NULL: v of each pool entry; an entry
+ *             whose position has no page in [0, num_pages) gets -inf.
+ * ws          workspace of csa2_reindex_workspace_size(batch, P, K).
+ * Errors: as csa2_reindex, and CSA2_E_NULL for key_scales.
+ */
+int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const float* key_scales,
+                        const int32_t* pool, const int32_t* pool_count, int32_t P, int32_t K,
+                        int32_t* out_idx, int32_t* out_count, float* out_values, void* ws,
+                        size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

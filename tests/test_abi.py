@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -95,3 +95,21 @@ def test_shard_calls_validate_before_launch(L):
     assert L.csa2_lse_merge(2, 8, 64, 384, 1, 1, 1, None, None) == -3
     assert L.csa2_lse_merge(0, 8, 64, 512, 1, 1, 1, None, None) == -2
 
+
+
+def test_scaled_calls_validate_before_launch(L):
+    c = _cache()
+    P = ctypes.pointer
+    # store_key_scales: negative count, null input
+    assert L.csa2_store_key_scales(P(c), -1, 1, 1, 1, 1, None) == -2
+    assert L.csa2_store_key_scales(P(c), 4, 1, 1, 1, None, None) == -1
+    assert L.csa2_store_key_scales(P(c), 0, None, None, None, None, None) == 0   # nothing to do
+    # index_topk_scaled: null scales, K out of range, short workspace
+    assert L.csa2_index_topk_scaled(P(c), 1, 100, 1, None, 8, 1, 1, None, None, 1, 1 << 30,
+                                    None) == -1
+    assert L.csa2_index_topk_scaled(P(c), 1, 100, 1, 1, -1, 1, 1, None, None, 1, 1 << 30,
+                                    None) == -2
+    assert L.csa2_index_topk_scaled(P(c), 1, 100, 1, 1, 8, 1, 1, None, None, 1, 16, None) == -4
+    # reindex_scaled: null scales, K > P
+    assert L.csa2_reindex_scaled(P(c), 1, None, 1, 1, 10, 8, 1, 1, None, 1, 1 << 30, None) == -1
+    assert L.csa2_reindex_scaled(P(c), 1, 1, 1, 1, 10, 20, 1, 1, None, 1, 1 << 30, None) == -2
