@@ -194,7 +194,18 @@ class Setup:
         self.csa2.sparse_decode(self.caches[r], self.ctx, self.q, self.sigma, self.idx, self.cnt,
                                 self.rings[r], self.ws_d, out=self.out, lse=self.lse)
 
+    def append_index_topk(self, r):
+        self.csa2.append_index_topk(self.caches[r], self.xd, self.seq, self.pos, self.kd,
+                                    self.rings[r], self.ctx, self.max_ctx, self.q_idx, self.wl.K,
+                                    self.ws_t, out_idx=self.idx, out_count=self.cnt)
+
     def step(self, r):
+        """One decode step: the append fused into the Full layer's selection, then attention."""
+        self.append_index_topk(r)
+        self.decode(r)
+
+    def step_unfused(self, r):
+        """The same step as three separate calls."""
         self.append(r)
         self.index_topk(r)
         self.decode(r)
@@ -427,7 +438,9 @@ def gpu_bench(args, S: Setup):
 
     # per-call durations: graphs of one call kind over the replicas
     calls = {name: time_call(S, fn, R) for name, fn in (
-        ("append", S.append), ("index_topk", S.index_topk), ("sparse_decode", S.decode))}
+        ("append", S.append), ("index_topk", S.index_topk),
+        ("append_index_topk", S.append_index_topk), ("sparse_decode", S.decode),
+        ("step_unfused", S.step_unfused))}
     torch.cuda.synchronize()
     for t, r in zip((S.idx, S.cnt, S.out, S.lse), ref):
         assert torch.equal(t, r), "per-call replay differs from the eager step"
@@ -633,8 +646,8 @@ def cpu_baseline(S: Setup, seconds: float):
 
 # ------------------------------------------------------------------ counters
 CALIB_BYTES = 1 << 30
-STEP_KERNELS = {"index_topk": ("index_score_kernel", "select_single_kernel", "select_filter_kernel",
-                               "select_final_kernel"),
+STEP_KERNELS = {"append_index_topk": ("append_score_kernel", "select_single_kernel",
+                                      "select_filter_kernel", "select_final_kernel"),
                 "sparse_decode": ("sparse_decode_kernel", "sparse_combine_kernel"),
                 "append": ("quantize_append_kernel",)}
 
@@ -748,12 +761,13 @@ def main() -> int:
     step_bytes = sum(nbytes.values())
     step_s = ev_ms * 1e-3 / args.steps
     gbs = step_bytes / step_s / 1e9
-    topk_s = calls["index_topk"] * 1e-6
-    topk_gbs = nbytes["index_topk"] / topk_s / 1e9
+    topk_gbs = nbytes["index_topk"] / (calls["index_topk"] * 1e-6) / 1e9
+    fused_bytes = nbytes["index_topk"] + nbytes["append"]
+    fused_gbs = fused_bytes / (calls["append_index_topk"] * 1e-6) / 1e9
     dec_gbs = nbytes["sparse_decode"] / (calls["sparse_decode"] * 1e-6) / 1e9
     dec_flops = 4 * H * D * (K + 128) * B                 # QK^T and PV over selected + window
     dec_tflops = dec_flops / (calls["sparse_decode"] * 1e-6) / 1e12
-    traffic = measured_traffic("index_topk")
+    traffic = measured_traffic("append_index_topk")
     res = {
         "metric": "decode attention queries/sec and achieved HBM GB/s (% of peak) at 64K ctx",
         "value": B * args.steps / wall,
@@ -771,14 +785,17 @@ def main() -> int:
                                "FP4 E2M1/E4M3-per-16 KV (288 B/token), int8 indexer dim 128, "
                                "Top-K 2048 outside the last 128, bf16 SWA 128",
                    "batch": B, "ctx": L, "heads": H, "head_dim": D, "idx_dim": Di, "top_k": K,
-                   "window": 128, "step": "quantize_append(1 token/seq) + index_topk + sparse_decode",
+                   "window": 128,
+                   "step": "append_index_topk (the 1-token/seq quantize_append fused into the Full "
+                           "layer's scoring launch, then the Top-K) + sparse_decode",
                    "replicas": args.replicas, "timing": "HIP graph replays"},
         "hbm_gbs": gbs,
         "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
         "step_bytes": step_bytes,
         "step_us_events": step_s * 1e6,
         "calls_us": calls,
-        "calls_gbs": {"index_topk": topk_gbs, "sparse_decode": dec_gbs},
+        "calls_gbs": {"index_topk": topk_gbs, "append_index_topk": fused_gbs,
+                      "sparse_decode": dec_gbs},
         "step_us_spread": spread,
         "sparse_decode_mfma": {"flops_per_call": dec_flops, "tflops": dec_tflops,
                                "peak_tflops": MFMA_F16_PEAK_TFLOPS,
@@ -786,11 +803,12 @@ def main() -> int:
         "copy_reference_gbs": copy_rate,
         "chain": chain,
         "scaled_indexer": scaled,
-        "roofline": {"kernel": "csa2_index_topk (" + ", ".join(STEP_KERNELS["index_topk"]) + ")",
-                     "bound": "hbm", "achieved": topk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": topk_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "frac_of_copy_reference": topk_gbs / copy_rate,
-                     "launch_us": calls["index_topk"], "bytes_per_launch": nbytes["index_topk"]},
+        "roofline": {"kernel": "csa2_append_index_topk ("
+                               + ", ".join(STEP_KERNELS["append_index_topk"]) + ")",
+                     "bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac_of_copy_reference": fused_gbs / copy_rate,
+                     "launch_us": calls["append_index_topk"], "bytes_per_launch": fused_bytes},
         "parity": parity,
     }
     if not args.no_cpu_baseline:

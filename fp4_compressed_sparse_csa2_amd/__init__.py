@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     Cache,
     Csa2Error,
     Workspace,
+    append_index_topk,
     index_topk,
     index_topk_range,
     index_topk_scaled,

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
                                                _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_lse_merge": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                               _c_vp, _c_vp]),
+            "csa2_append_index_topk": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                      _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp,
+                                                      _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
             "csa2_index_topk_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
@@ -223,6 +226,47 @@ def index_topk(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.T
                                  q_idx.data_ptr(), K, out_idx.data_ptr(), out_count.data_ptr(),
                                  _ptr(out_scores), w.data_ptr(), w.numel(), _stream(dev)),
            "csa2_index_topk")
+    return out_idx, out_count
+
+
+def append_index_topk(cache: Cache, x: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                      keys: torch.Tensor | None, swa: torch.Tensor | None, ctx_len: torch.Tensor,
+                      max_ctx: int, q_idx: torch.Tensor, K: int, ws: Workspace,
+                      out_idx: torch.Tensor | None = None, out_count: torch.Tensor | None = None,
+                      out_scores: torch.Tensor | None = None):
+    """quantize_append of decode tokens (each inside its sequence's window)
+    and the Full layer's index_topk in one call.  Returns (idx [B, K], count [B])."""
+    x = _as_u16(x)
+    n = x.shape[0]
+    dev, B = cache.device, cache.batch
+    _need(x, "x", torch.uint16, dev, (n, cache.head_dim))
+    _need(seq, "seq", torch.int32, dev, (n,))
+    _need(pos, "pos", torch.int32, dev, (n,))
+    if keys is not None:
+        _need(keys, "keys", torch.int8, dev, (n, cache.idx_dim))
+    if swa is not None:
+        swa = _as_u16(swa)
+        _need(swa, "swa", torch.uint16, dev, (B, WINDOW, cache.head_dim))
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.int32, dev, (B, max_ctx))
+    nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
+    if nbytes == 0:
+        raise Csa2Error(f"append_index_topk: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_append_index_topk(ctypes.byref(cache.struct), n, x.data_ptr(), _ptr(keys),
+                                        seq.data_ptr(), pos.data_ptr(), _ptr(swa),
+                                        ctx_len.data_ptr(), max_ctx, q_idx.data_ptr(), K,
+                                        out_idx.data_ptr(), out_count.data_ptr(),
+                                        _ptr(out_scores), w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_append_index_topk")
     return out_idx, out_count
 
 

@@ -3,6 +3,7 @@
 // reads of device memory on the host.
 #include "csa2.h"
 
+#include "append.h"
 #include "common.h"
 #include "launch.h"
 
@@ -109,6 +110,27 @@ int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max
   return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, nullptr, K, 0,
                                         kMaxCtx, out_idx, out_count, out_scores, nullptr, ws,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int csa2_append_index_topk(const csa2_cache* cache, int32_t n_tokens, const uint16_t* x,
+                           const int8_t* key_i8, const int32_t* seq, const int32_t* pos,
+                           uint16_t* swa, const int32_t* ctx_len, int32_t max_ctx,
+                           const int8_t* q_idx, int32_t K, int32_t* out_idx, int32_t* out_count,
+                           int32_t* out_scores, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (n_tokens < 0) return CSA2_E_SHAPE;
+  if (n_tokens > 0 && (x == nullptr || seq == nullptr || pos == nullptr)) return CSA2_E_NULL;
+  if (ctx_len == nullptr || q_idx == nullptr || out_count == nullptr) return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
+  const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  const CacheArgs c = args_of(cache);
+  const csa2::AppendArgs ap = csa2::append_args(c, n_tokens, x, key_i8, seq, pos, swa);
+  return status_of(csa2::run_index_topk(c, ctx_len, max_ctx, q_idx, nullptr, K, 0, kMaxCtx,
+                                        out_idx, out_count, out_scores, nullptr, ws,
+                                        static_cast<hipStream_t>(stream), &ap));
 }
 
 int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float* scale,

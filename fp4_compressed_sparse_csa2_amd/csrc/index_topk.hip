@@ -15,6 +15,7 @@
 // pages pair the indexer keys with a scale), stored [page][row] beside the
 // cache; the ranked value is fl32(s_p * score_p), kept as a 32-bit order key
 // whose top 11 bits feed the same histogram.
+#include "append.h"
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -46,20 +47,44 @@ __device__ __forceinline__ int seq_candidates(const int32_t* ctx_len, int b, int
 }
 
 // ------------------------------------------------------------------ score
+struct ScoreArgs {
+  const uint8_t* pages;
+  const int32_t* page_table;
+  int num_pages;
+  int max_pages;
+  int keys_off;
+  int page_bytes;
+  const int32_t* ctx_len;
+  int max_ctx;
+  int p_begin;
+  int p_end;
+  const int8_t* q_idx;
+  const float* key_scales;    // scaled variant only
+  int K;
+  int32_t* scores;
+  int32_t* out_scores;
+  uint32_t* ctrl;
+};
+
+// Score block `chunk` of sequence b (hist: kBins words of LDS).
 template <int DI, bool SCALED>
-__global__ __launch_bounds__(kBlock) void index_score_kernel(
-    const uint8_t* __restrict__ pages, const int32_t* __restrict__ page_table, int num_pages,
-    int max_pages, int keys_off, int page_bytes, const int32_t* __restrict__ ctx_len,
-    int max_ctx, int p_begin, int p_end, const int8_t* __restrict__ q_idx,
-    const float* __restrict__ key_scales, int K,
-    int32_t* __restrict__ scores, int32_t* __restrict__ out_scores, uint32_t* __restrict__ ctrl) {
+__device__ __forceinline__ void score_block(const ScoreArgs& sa, int chunk, int b,
+                                            uint32_t* hist) {
   constexpr int LPP = DI / 16;        // lanes per position (16 key bytes each)
   constexpr int PPL = 64 / LPP;       // positions per 1 KB wave load
-  __shared__ uint32_t hist[kBins];
+  const uint8_t* __restrict__ pages = sa.pages;
+  const int32_t* __restrict__ page_table = sa.page_table;
+  const int num_pages = sa.num_pages, max_pages = sa.max_pages, keys_off = sa.keys_off;
+  const int page_bytes = sa.page_bytes, max_ctx = sa.max_ctx, p_begin = sa.p_begin;
+  const int8_t* __restrict__ q_idx = sa.q_idx;
+  const float* __restrict__ key_scales = sa.key_scales;
+  const int K = sa.K;
+  int32_t* __restrict__ scores = sa.scores;
+  int32_t* __restrict__ out_scores = sa.out_scores;
+  uint32_t* __restrict__ ctrl = sa.ctrl;
 
-  const int b = blockIdx.y;
-  const int n = seq_candidates(ctx_len, b, max_ctx, max_pages, p_begin, p_end);
-  const int chunk0 = blockIdx.x * kChunk;
+  const int n = seq_candidates(sa.ctx_len, b, max_ctx, max_pages, p_begin, sa.p_end);
+  const int chunk0 = chunk * kChunk;
   if (chunk0 >= n) return;
   const bool do_hist = K > 0 && n > K;
 
@@ -148,6 +173,25 @@ __global__ __launch_bounds__(kBlock) void index_score_kernel(
   }
 }
 
+template <int DI, bool SCALED>
+__global__ __launch_bounds__(kBlock) void index_score_kernel(ScoreArgs sa) {
+  __shared__ uint32_t hist[kBins];
+  score_block<DI, SCALED>(sa, blockIdx.x, blockIdx.y, hist);
+}
+
+// The Full layer's append fused into its scoring grid: rows 0..batch-1 of
+// the grid score, row `batch` appends (tokens at scoring candidates are
+// skipped, so no append write overlaps a scoring read).
+template <int D, int DI>
+__global__ __launch_bounds__(kBlock) void append_score_kernel(ScoreArgs sa, AppendArgs ap) {
+  __shared__ uint32_t hist[kBins];
+  if ((int)blockIdx.y == ap.batch) {
+    append_block<D, DI>(ap, blockIdx.x);
+    return;
+  }
+  score_block<DI, false>(sa, blockIdx.x, blockIdx.y, hist);
+}
+
 // ------------------------------------------------------------------ host
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -169,21 +213,20 @@ size_t index_topk_ws_bytes(int batch, int max_ctx, int /*K*/) {
   return topk_ws(batch, max_ctx).total;
 }
 
-template <int DI, bool SCALED>
-static void launch_score(const dim3& grid, hipStream_t st, const CacheArgs& c,
-                         const PageLayout& lay, const int32_t* ctx_len, int max_ctx, int p_begin,
-                         int p_end, const int8_t* q_idx, const float* key_scales, int K,
-                         int32_t* scores, int32_t* out_scores, uint32_t* ctrl) {
-  hipLaunchKernelGGL((index_score_kernel<DI, SCALED>), grid, dim3(kBlock), 0, st,
-                     (const uint8_t*)c.pages, c.page_table, c.num_pages, c.max_pages,
-                     lay.keys_off, lay.page_bytes, ctx_len, max_ctx, p_begin, p_end, q_idx,
-                     key_scales, K, scores, out_scores, ctrl);
+template <int D, int DI>
+static void launch_append_score(const dim3& grid, hipStream_t st, const ScoreArgs& sa,
+                                const AppendArgs& ap) {
+  const int app_blocks =
+      (ap.n_tokens + append_tokens_per_block<D>() - 1) / append_tokens_per_block<D>();
+  const dim3 g(grid.x > (unsigned)app_blocks ? grid.x : (unsigned)app_blocks, grid.y + 1);
+  hipLaunchKernelGGL((append_score_kernel<D, DI>), g, dim3(kBlock), 0, st, sa, ap);
 }
 
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
                           const int8_t* q_idx, const float* key_scales, int K, int p_begin,
                           int p_end, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
-                          int32_t* out_sel_scores, void* ws, hipStream_t st) {
+                          int32_t* out_sel_scores, void* ws, hipStream_t st,
+                          const AppendArgs* append) {
   const TopkWs w = topk_ws(c.batch, max_ctx);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + w.ctrl);
@@ -195,18 +238,41 @@ hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ct
   const int n_chunks = (max_entries + kChunk - 1) / kChunk;
   const dim3 grid(n_chunks > 0 ? n_chunks : 1, c.batch);
   const bool scaled = key_scales != nullptr;
-  if (c.Di == 128 && !scaled)
-    launch_score<128, false>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx, nullptr,
-                             K, scores, out_scores, ctrl);
-  else if (c.Di == 128)
-    launch_score<128, true>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx,
-                            key_scales, K, scores, out_scores, ctrl);
-  else if (!scaled)
-    launch_score<64, false>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx, nullptr,
-                            K, scores, out_scores, ctrl);
-  else
-    launch_score<64, true>(grid, st, c, lay, ctx_len, max_ctx, p_begin, p_end, q_idx,
-                           key_scales, K, scores, out_scores, ctrl);
+  ScoreArgs sa;
+  sa.pages = static_cast<const uint8_t*>(c.pages);
+  sa.page_table = c.page_table;
+  sa.num_pages = c.num_pages;
+  sa.max_pages = c.max_pages;
+  sa.keys_off = lay.keys_off;
+  sa.page_bytes = lay.page_bytes;
+  sa.ctx_len = ctx_len;
+  sa.max_ctx = max_ctx;
+  sa.p_begin = p_begin;
+  sa.p_end = p_end;
+  sa.q_idx = q_idx;
+  sa.key_scales = key_scales;
+  sa.K = K;
+  sa.scores = scores;
+  sa.out_scores = out_scores;
+  sa.ctrl = ctrl;
+  if (append != nullptr && append->n_tokens > 0) {
+    AppendArgs ap = *append;
+    ap.ctx_len = ctx_len;
+    ap.max_ctx = max_ctx;
+#define AS_CASE(D_, DI_) \
+    if (c.D == D_ && c.Di == DI_) launch_append_score<D_, DI_>(grid, st, sa, ap);
+    AS_CASE(128, 64) AS_CASE(128, 128) AS_CASE(256, 64) AS_CASE(256, 128)
+    AS_CASE(512, 64) AS_CASE(512, 128)
+#undef AS_CASE
+  } else if (c.Di == 128 && !scaled) {
+    hipLaunchKernelGGL((index_score_kernel<128, false>), grid, dim3(kBlock), 0, st, sa);
+  } else if (c.Di == 128) {
+    hipLaunchKernelGGL((index_score_kernel<128, true>), grid, dim3(kBlock), 0, st, sa);
+  } else if (!scaled) {
+    hipLaunchKernelGGL((index_score_kernel<64, false>), grid, dim3(kBlock), 0, st, sa);
+  } else {
+    hipLaunchKernelGGL((index_score_kernel<64, true>), grid, dim3(kBlock), 0, st, sa);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelectArgs a;

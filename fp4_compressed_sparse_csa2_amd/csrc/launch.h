@@ -19,6 +19,10 @@ struct CacheArgs {
 
 hipError_t run_fill_zero(void* ws, size_t bytes, hipStream_t st);
 
+struct AppendArgs;   // append.h
+AppendArgs append_args(const CacheArgs& c, int n, const uint16_t* x, const int8_t* key,
+                       const int32_t* seq, const int32_t* pos, uint16_t* swa);
+
 // One selection call over per-sequence int32 scores, or float order keys
 // (float_keys != 0; see select.hip).  The
 // entries of sequence b are 0 <= i < n_b with n_b from ctx_len (candidates
@@ -55,10 +59,13 @@ hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, con
 // scales; the ranked values are then scaled_value(score, scale) and the
 // score outputs carry float bits.
 size_t index_topk_ws_bytes(int batch, int max_ctx, int K);
+// append: NULL, or the tokens of a decode append (int32 scores only) fused
+// into the scoring launch; tokens at scoring candidates are skipped.
 hipError_t run_index_topk(const CacheArgs& c, const int32_t* ctx_len, int max_ctx,
                           const int8_t* q_idx, const float* key_scales, int K, int p_begin,
                           int p_end, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
-                          int32_t* out_sel_scores, void* ws, hipStream_t st);
+                          int32_t* out_sel_scores, void* ws, hipStream_t st,
+                          const AppendArgs* append = nullptr);
 
 size_t reindex_ws_bytes(int batch, int P, int K);
 hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const float* key_scales,

@@ -171,6 +171,23 @@ int csa2_index_topk(const csa2_cache* cache, const int32_t* ctx_len, int32_t max
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_append_index_topk -- a decode step's append and the Full layer's
+ * selection in one call: the same results as csa2_quantize_append(cache,
+ * n_tokens, x, key_i8, seq, pos, swa) followed by csa2_index_topk(cache,
+ * ctx_len, max_ctx, q_idx, K, ...), for tokens that lie in their sequence's
+ * window (L - 128 <= pos, L = ctx_len[seq] clamped as in csa2_index_topk).
+ * The append runs inside the scoring launch, which reads only positions
+ * below L - 128, so the two cannot race; a token at a position below
+ * L - 128 (a scoring candidate) is not written.  Arguments, limits, outputs
+ * and errors as the two calls; ws is csa2_index_topk's workspace.
+ */
+int csa2_append_index_topk(const csa2_cache* cache, int32_t n_tokens, const uint16_t* x,
+                           const int8_t* key_i8, const int32_t* seq, const int32_t* pos,
+                           uint16_t* swa, const int32_t* ctx_len, int32_t max_ctx,
+                           const int8_t* q_idx, int32_t K, int32_t* out_idx, int32_t* out_count,
+                           int32_t* out_scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa2_reindex -- Reindex layer: refilter the owner's candidate pool.
  * Source: hierarchical sparse indexer, later indexer layers refilter only
  * inside the pool built by the first Full layer (neodrop.ai V4.1-Flash

@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -113,3 +113,17 @@ def test_scaled_calls_validate_before_launch(L):
     # reindex_scaled: null scales, K > P
     assert L.csa2_reindex_scaled(P(c), 1, None, 1, 1, 10, 8, 1, 1, None, 1, 1 << 30, None) == -1
     assert L.csa2_reindex_scaled(P(c), 1, 1, 1, 1, 10, 20, 1, 1, None, 1, 1 << 30, None) == -2
+
+
+def test_append_index_topk_validates_before_launch(L):
+    c = _cache()
+    P = ctypes.pointer
+    # negative token count, null token input, K out of range, short workspace
+    assert L.csa2_append_index_topk(P(c), -1, 1, None, 1, 1, None, 1, 100, 1, 8, 1, 1, None, 1,
+                                    1 << 30, None) == -2
+    assert L.csa2_append_index_topk(P(c), 4, None, None, 1, 1, None, 1, 100, 1, 8, 1, 1, None, 1,
+                                    1 << 30, None) == -1
+    assert L.csa2_append_index_topk(P(c), 4, 1, None, 1, 1, None, 1, 100, 1, -1, 1, 1, None, 1,
+                                    1 << 30, None) == -2
+    assert L.csa2_append_index_topk(P(c), 4, 1, None, 1, 1, None, 1, 100, 1, 8, 1, 1, None, 1,
+                                    16, None) == -4
