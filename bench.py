@@ -75,6 +75,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the chain, schedule and scaled-indexer timings (profiling runs: "
+                         "only the step's kernels and their per-call timings are launched)")
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: three 1 GiB device copies (the counter "
                          "calibration), then --warmup + --steps eager steps; no timing")
@@ -648,8 +651,7 @@ def cpu_baseline(S: Setup, seconds: float):
 CALIB_BYTES = 1 << 30
 STEP_KERNELS = {"append_index_topk": ("append_score_kernel", "select_single_kernel",
                                       "select_filter_kernel", "select_final_kernel"),
-                "sparse_decode": ("sparse_decode_kernel", "sparse_combine_kernel"),
-                "append": ("quantize_append_kernel",)}
+                "sparse_decode": ("sparse_decode_kernel", "sparse_combine_kernel")}
 
 
 def counter_run(args) -> int:
@@ -752,9 +754,11 @@ def main() -> int:
     S = Setup(args.replicas)
     wl = S.wl
     wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
-    chain = chain_calls(S)
-    chain["schedule"] = schedule_calls(S)
-    scaled = scaled_calls(S)
+    chain = scaled = None
+    if not args.no_extras:
+        chain = chain_calls(S)
+        chain["schedule"] = schedule_calls(S)
+        scaled = scaled_calls(S)
     copy_rate = copy_gbs(torch)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
