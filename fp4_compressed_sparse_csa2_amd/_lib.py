@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                                       _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp,
                                                       _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+            "csa2_store_key_scales_e4m3": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                          _c_vp]),
             "csa2_index_topk_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
                                                       _c_vp]),
@@ -345,18 +347,20 @@ def key_scales_for(cache: Cache) -> torch.Tensor:
 
 def store_key_scales(cache: Cache, scale: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
                      key_scales: torch.Tensor) -> None:
-    """Write the fp32 key scales of tokens at (seq, pos) into key_scales
-    [num_pages, 64] through the page table."""
+    """Write the key scales of tokens at (seq, pos) into key_scales
+    [num_pages, 64] through the page table: fp32 scales, or E4M3 bytes
+    (uint8, decoded exactly)."""
     dev = cache.device
     n = scale.shape[0]
-    _need(scale, "scale", torch.float32, dev, (n,))
+    e4m3 = scale.dtype == torch.uint8
+    _need(scale, "scale", torch.uint8 if e4m3 else torch.float32, dev, (n,))
     _need(seq, "seq", torch.int32, dev, (n,))
     _need(pos, "pos", torch.int32, dev, (n,))
     _need(key_scales, "key_scales", torch.float32, dev, (cache.pages.shape[0], PAGE_TOKENS))
-    _check(lib().csa2_store_key_scales(ctypes.byref(cache.struct), n, scale.data_ptr(),
-                                       seq.data_ptr(), pos.data_ptr(), key_scales.data_ptr(),
-                                       _stream(dev)),
-           "csa2_store_key_scales")
+    fn = lib().csa2_store_key_scales_e4m3 if e4m3 else lib().csa2_store_key_scales
+    _check(fn(ctypes.byref(cache.struct), n, scale.data_ptr(), seq.data_ptr(), pos.data_ptr(),
+              key_scales.data_ptr(), _stream(dev)),
+           "csa2_store_key_scales" + ("_e4m3" if e4m3 else ""))
 
 
 def index_topk_scaled(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,

@@ -133,17 +133,29 @@ int csa2_append_index_topk(const csa2_cache* cache, int32_t n_tokens, const uint
                                         static_cast<hipStream_t>(stream), &ap));
 }
 
-int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float* scale,
-                          const int32_t* seq, const int32_t* pos, float* key_scales,
-                          void* stream) {
+static int store_key_scales(const csa2_cache* cache, int32_t n_tokens, const void* scale,
+                            bool e4m3, const int32_t* seq, const int32_t* pos, float* key_scales,
+                            void* stream) {
   int st = check_cache(cache);
   if (st != CSA2_OK) return st;
   if (n_tokens < 0) return CSA2_E_SHAPE;
   if (n_tokens > 0 && (scale == nullptr || seq == nullptr || pos == nullptr ||
                        key_scales == nullptr))
     return CSA2_E_NULL;
-  return status_of(csa2::run_store_key_scales(args_of(cache), n_tokens, scale, seq, pos,
+  return status_of(csa2::run_store_key_scales(args_of(cache), n_tokens, scale, e4m3, seq, pos,
                                               key_scales, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float* scale,
+                          const int32_t* seq, const int32_t* pos, float* key_scales,
+                          void* stream) {
+  return store_key_scales(cache, n_tokens, scale, false, seq, pos, key_scales, stream);
+}
+
+int csa2_store_key_scales_e4m3(const csa2_cache* cache, int32_t n_tokens,
+                               const uint8_t* scale_e4m3, const int32_t* seq, const int32_t* pos,
+                               float* key_scales, void* stream) {
+  return store_key_scales(cache, n_tokens, scale_e4m3, true, seq, pos, key_scales, stream);
 }
 
 int csa2_index_topk_scaled(const csa2_cache* cache, const int32_t* ctx_len, int32_t max_ctx,

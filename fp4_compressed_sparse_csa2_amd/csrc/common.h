@@ -131,6 +131,12 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return e == 0 ? (float)m * (1.0f / 512.0f) : __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// Value of any E4M3 (FN) byte: the sign applied, NaN for S.1111.111.
+__device__ __forceinline__ float e4m3_signed_value(uint32_t b) {
+  const float v = (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : e4m3_value(b & 0x7Fu);
+  return (b & 0x80u) ? -v : v;
+}
+
 // E4M3 code of q >= 0: nearest value, ties to the even code, saturating at
 // 448 (0x7E).  q = amax/6 is never within a few ulps of an E4M3 midpoint
 // unless it equals it (amax has 8 significant bits, 6*midpoint at most 8), so

@@ -73,7 +73,8 @@ hipError_t run_reindex(const CacheArgs& c, const int8_t* q_idx, const float* key
                        int32_t* out_idx, int32_t* out_count, int32_t* out_scores, void* ws,
                        hipStream_t st);
 
-hipError_t run_store_key_scales(const CacheArgs& c, int n, const float* scale,
+// scale: float [n], or E4M3 bytes [n] when e4m3 (decoded exactly to fp32)
+hipError_t run_store_key_scales(const CacheArgs& c, int n, const void* scale, bool e4m3,
                                 const int32_t* seq, const int32_t* pos, float* key_scales,
                                 hipStream_t st);
 

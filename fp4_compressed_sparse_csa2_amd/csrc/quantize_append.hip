@@ -50,12 +50,14 @@ hipError_t run_quantize_append(const CacheArgs& c, int n, const uint16_t* x, con
   return hipErrorInvalidValue;
 }
 
-// Key scales of appended tokens: scale[i] goes to key_scales[pg][p % 64] for
-// token i at (seq[i], pos[i]) with pg its page; tokens that do not map to a
-// page are skipped, as in the append above.
+// Key scales of appended tokens: scale[i] (fp32, or an E4M3 byte decoded
+// exactly) goes to key_scales[pg][p % 64] for token i at (seq[i], pos[i])
+// with pg its page; tokens that do not map to a page are skipped, as in the
+// append above.
+template <bool E4M3>
 __global__ __launch_bounds__(kBlock) void store_key_scales_kernel(
     const int32_t* __restrict__ page_table, int num_pages, int max_pages, int batch, int n,
-    const float* __restrict__ scale, const int32_t* __restrict__ seq,
+    const void* __restrict__ scale, const int32_t* __restrict__ seq,
     const int32_t* __restrict__ pos, float* __restrict__ key_scales) {
   const int i = blockIdx.x * kBlock + threadIdx.x;
   if (i >= n) return;
@@ -63,16 +65,22 @@ __global__ __launch_bounds__(kBlock) void store_key_scales_kernel(
   if (b < 0 || b >= batch || p < 0 || p >= max_pages * kPage) return;
   const int pg = page_table[(size_t)b * max_pages + p / kPage];
   if (pg < 0 || pg >= num_pages) return;
-  key_scales[(size_t)pg * kPage + p % kPage] = scale[i];
+  const float s = E4M3 ? e4m3_signed_value(static_cast<const uint8_t*>(scale)[i])
+                       : static_cast<const float*>(scale)[i];
+  key_scales[(size_t)pg * kPage + p % kPage] = s;
 }
 
-hipError_t run_store_key_scales(const CacheArgs& c, int n, const float* scale,
+hipError_t run_store_key_scales(const CacheArgs& c, int n, const void* scale, bool e4m3,
                                 const int32_t* seq, const int32_t* pos, float* key_scales,
                                 hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(store_key_scales_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0,
-                     st, c.page_table, c.num_pages, c.max_pages, c.batch, n, scale, seq, pos,
-                     key_scales);
+  const dim3 grid((n + kBlock - 1) / kBlock);
+  if (e4m3)
+    hipLaunchKernelGGL(store_key_scales_kernel<true>, grid, dim3(kBlock), 0, st, c.page_table,
+                       c.num_pages, c.max_pages, c.batch, n, scale, seq, pos, key_scales);
+  else
+    hipLaunchKernelGGL(store_key_scales_kernel<false>, grid, dim3(kBlock), 0, st, c.page_table,
+                       c.num_pages, c.max_pages, c.batch, n, scale, seq, pos, key_scales);
   return hipGetLastError();
 }
 

@@ -188,6 +188,12 @@ def key_scales(wl: Workload, b: int, n: int, mode: str = "lognormal") -> np.ndar
     return s
 
 
+def key_scales_e4m3(wl: Workload, b: int, n: int) -> np.ndarray:
+    """Per-token indexer-key scales as E4M3 bytes, uint8 [n]: codes
+    U{0x00..0x7E} (every finite non-negative value, zero included)."""
+    return _rng(wl, T_KSCALE, 1, b).integers(0, 0x7E, size=n, endpoint=True).astype(np.uint8)
+
+
 def query(wl: Workload, layer: int = 0) -> np.ndarray:
     """Attention queries, bf16(N(0,1) * std) with std = 1/sqrt(D) by default:
     uint16 [B, H, D]."""

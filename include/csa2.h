@@ -352,6 +352,18 @@ int csa2_store_key_scales(const csa2_cache* cache, int32_t n_tokens, const float
                           void* stream);
 
 /*
+ * csa2_store_key_scales_e4m3 -- the same with one E4M3 byte per token (the
+ * OCP "FN" encoding of the cache's own scales): each byte is decoded exactly
+ * to fp32 (an E4M3 value is a float32 value), so the ranking is that of the
+ * decoded scales.  The NaN codes 0x7F / 0xFF decode to NaN, which the
+ * ranking takes as a non-finite scale.
+ * scale_e4m3 device uint8 [n_tokens]; other arguments and errors as above.
+ */
+int csa2_store_key_scales_e4m3(const csa2_cache* cache, int32_t n_tokens,
+                               const uint8_t* scale_e4m3, const int32_t* seq, const int32_t* pos,
+                               float* key_scales, void* stream);
+
+/*
  * csa2_index_topk_scaled -- csa2_index_topk ranked by the scaled values v_p.
  * out_idx / out_count as csa2_index_topk (the first min(K, n) candidates in
  * (value descending, position ascending) order, ascending, -1 padded).

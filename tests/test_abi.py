@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -104,6 +104,8 @@ def test_scaled_calls_validate_before_launch(L):
     assert L.csa2_store_key_scales(P(c), -1, 1, 1, 1, 1, None) == -2
     assert L.csa2_store_key_scales(P(c), 4, 1, 1, 1, None, None) == -1
     assert L.csa2_store_key_scales(P(c), 0, None, None, None, None, None) == 0   # nothing to do
+    assert L.csa2_store_key_scales_e4m3(P(c), -1, 1, 1, 1, 1, None) == -2
+    assert L.csa2_store_key_scales_e4m3(P(c), 4, None, 1, 1, 1, None) == -1
     # index_topk_scaled: null scales, K out of range, short workspace
     assert L.csa2_index_topk_scaled(P(c), 1, 100, 1, None, 8, 1, 1, None, None, 1, 1 << 30,
                                     None) == -1

@@ -15,6 +15,7 @@ import torch
 
 import fp4_compressed_sparse_csa2_amd as csa2
 from harness import gen
+from oracle import formats as OF
 from oracle import select as OS
 
 from gpu_common import DEV, GpuCache, log, to_dev, to_host
@@ -182,6 +183,32 @@ def test_reindex_scaled(mode, K_full, K2):
         assert np.array_equal(vals[b, :c].view(np.uint32), v.view(np.uint32)), f"b={b}"
         want, wcnt = OS.reindex_values(pool[b], c, v, K2)
         assert int(cnt[b]) == wcnt and np.array_equal(idx[b], want), f"b={b}"
+
+
+def test_e4m3_scales():
+    """E4M3 scale bytes: stored as their exact fp32 values, then ranked."""
+    wl = gen.WORKLOADS["b128_rag"].with_(B=6, L=30000, L_min=1, D=128, H=16, Di=64)
+    log("scaled e4m3 store + topk")
+    gc = GpuCache(wl, keep_kv=False)
+    ks = csa2.key_scales_for(gc.cache)
+    scales = []
+    want = np.zeros(tuple(ks.shape), np.float32)
+    for b in range(wl.B):
+        L = int(gc.lens[b])
+        codes = gen.key_scales_e4m3(wl, b, L)
+        s = OF.e4m3_value(codes).astype(np.float32)     # exact: E4M3 values are float32 values
+        scales.append(s)
+        p = np.arange(L)
+        want[gc.pt[b, p // gen.PAGE], p % gen.PAGE] = s
+        if L > 0:
+            csa2.store_key_scales(gc.cache, to_dev(codes),
+                                  torch.full((L,), b, dtype=torch.int32, device=DEV),
+                                  torch.arange(L, dtype=torch.int32, device=DEV), ks)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ks).view(np.uint32), want.view(np.uint32))
+    q = gen.idx_query(wl)
+    for K in (1, 300, 4000):
+        _check_topk(gc, q, ks, scales, K)
 
 
 def test_b8_64k_scaled():
