@@ -218,3 +218,39 @@ def test_b8_64k_scaled():
     gc = GpuCache(wl, keep_kv=False)
     ks, scales = _store_scales(gc, "lognormal")
     _check_topk(gc, gen.idx_query(wl), ks, scales, wl.K)
+
+
+def test_non_finite_scales_keep_the_output_well_formed():
+    """Non-finite scales give an unspecified order, never a fault: the output
+    is still count = min(K, n) distinct candidate positions, ascending, -1
+    padded."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=30000, Di=64)
+    log("scaled non-finite scales")
+    gc = GpuCache(wl, keep_kv=False)
+    ks, scales = _store_scales(gc, "lognormal")
+    bad = []
+    for b in range(wl.B):
+        L = int(gc.lens[b])
+        s = scales[b].copy()
+        r = np.random.default_rng(b)
+        sel = r.choice(L, size=300, replace=False)
+        s[sel[:100]] = np.inf
+        s[sel[100:200]] = -np.inf
+        s[sel[200:]] = np.nan
+        bad.append(s)
+        csa2.store_key_scales(gc.cache, to_dev(s), torch.full((L,), b, dtype=torch.int32, device=DEV),
+                              torch.arange(L, dtype=torch.int32, device=DEV), ks)
+    torch.cuda.synchronize()
+    q = gen.idx_query(wl)
+    for K in (100, 5000):
+        idx, cnt, _ = csa2.index_topk_scaled(gc.cache, gc.ctx, int(gc.lens.max()), to_dev(q), ks,
+                                             K, csa2.Workspace(DEV))
+        torch.cuda.synchronize()
+        idx, cnt = to_host(idx), to_host(cnt)
+        for b in range(wl.B):
+            n = int(gc.lens[b]) - gen.WINDOW
+            c = int(cnt[b])
+            assert c == min(K, n)
+            got = idx[b, :c]
+            assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < n
+            assert np.all(idx[b, c:] == -1)
