@@ -97,33 +97,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return base + x - v;
 }
 
-// The same over 64-bit values (two packed 32-bit counts whose sums stay
-// below 2^32 scan as one).  `scratch`: NT/64 long longs of shared memory.
-template <int NT = kBlock>
-__device__ __forceinline__ unsigned long long block_exclusive_scan64(unsigned long long v,
-                                                                     unsigned long long* scratch,
-                                                                     unsigned long long* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const unsigned long long y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  unsigned long long base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const unsigned long long t = scratch[w];
-    base += (w < wave) ? t : 0ull;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
 // ------------------------------------------------------------------ FP8 / FP4
 // Value of an E4M3 (OCP "FN") byte with the sign bit clear, as float (exact).
 __device__ __forceinline__ float e4m3_value(uint32_t b) {

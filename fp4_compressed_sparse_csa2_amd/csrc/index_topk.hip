@@ -31,7 +31,6 @@ constexpr int kChunk = kChunkPages * kPage;      // positions per score block
 constexpr int kPagesPerWave = kChunkPages / (kBlock / 64);
 static_assert(kPagesPerWave >= 1 && kChunkPages % (kBlock / 64) == 0, "whole pages per wave");
 
-constexpr int kCtrlHist1 = 0;                  // the top-digit histogram in the control words
 
 // Candidates of sequence b: positions p_begin <= p < min(p_end, L - 128);
 // entry i is position p_begin + i.
@@ -163,7 +162,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& sa, int chunk, int 
   }
   if (do_hist) {
     __syncthreads();
-    uint32_t* g = ctrl + (size_t)b * kCtrlWords + kCtrlHist1;
+    uint32_t* g = ctrl + (size_t)b * kCtrlWords + (chunk % kHistReps) * kBins;
     uint32_t h[kBins / kBlock];
 #pragma unroll
     for (int k = 0; k < kBins / kBlock; ++k) h[k] = hist[k * kBlock + threadIdx.x];

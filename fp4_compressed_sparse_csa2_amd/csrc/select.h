@@ -16,12 +16,19 @@
 namespace csa2 {
 
 // Per-sequence control words of a selection (uint32): the top-digit histogram
-// the scoring kernel fills (kBins words), the low-digit histogram of the
-// entries whose top digit is the threshold's (kBins words, filled by the
-// multi-block filter), then spare words.  The size does not depend on the
-// call's sizes, so a zeroed workspace stays zeroed between calls of any shape.
-constexpr int kCtrlWords = 2 * kBins + 64;
-constexpr int kCtrlHist2 = kBins;
+// the scoring kernel fills, as kHistReps replicas of kBins words that sum to
+// it (score block i adds into replica i % kHistReps, which spreads the
+// atomics on the busiest bins over two addresses), the low-digit histogram
+// of the entries whose top digit is the threshold's (kBins words, filled by
+// the multi-block filter), the top digit and the count above it as the
+// filter found them (two words), then spare words.  The size does not depend
+// on the call's sizes, so a zeroed workspace stays zeroed between calls of
+// any shape.
+constexpr int kHistReps = 2;
+constexpr int kCtrlHist2 = kHistReps * kBins;
+constexpr int kCtrlTop = kCtrlHist2 + kBins;
+constexpr int kCtrlWords = kCtrlTop + 64;
+static_assert(kCtrlWords % 4 == 0, "control words are cleared 16 bytes at a time");
 constexpr int kMaxSelChunks = 4096;      // 4096-entry filter chunks of a 2^24-entry sequence
 constexpr int kSingleMax = 1 << 14;      // longest sequence for the one-block selection
 
@@ -37,12 +44,18 @@ struct DigitBins {
   int h[BPT];
 };
 
-template <int NT = kBlock, typename HistT>
+// REPS > 1: the histogram is the sum of REPS replicas kBins words apart.
+template <int NT = kBlock, int REPS = 1, typename HistT>
 __device__ __forceinline__ DigitBins<NT> load_digit_bins(const HistT* hist) {
   DigitBins<NT> d;
   const int top = kBins - DigitBins<NT>::BPT * (int)threadIdx.x;
 #pragma unroll
   for (int k = 0; k < DigitBins<NT>::BPT; ++k) d.h[k] = (int)hist[top - 1 - k];
+#pragma unroll
+  for (int r = 1; r < REPS; ++r) {
+#pragma unroll
+    for (int k = 0; k < DigitBins<NT>::BPT; ++k) d.h[k] += (int)hist[r * kBins + top - 1 - k];
+  }
   return d;
 }
 
@@ -84,66 +97,6 @@ template <int NT = kBlock, typename HistT>
 __device__ void find_digit(const HistT* hist, int need, int* scan_scratch, int* t_out,
                            int* above_out) {
   find_digit_in<NT>(load_digit_bins<NT>(hist), need, scan_scratch, t_out, above_out);
-}
-
-// Both digits of the threshold from the two histograms at once:
-//   t1 = largest top digit with sum_{bin >= t1} h1 >= K, above1 = sum_{bin > t1} h1;
-//   t2 = largest low digit with sum_{bin >= t2} h2 >= K - above1,
-//   above2 = sum_{bin > t2} h2, where h2 counts the low digits of the entries
-//   whose top digit is t1.
-// One block scan of the packed pair of per-thread sums.  Results in
-// sh[0..3] = t1, above1, t2, above2 (t1 = -1 / t2 = -1 when not found),
-// visible to every thread on return.  All threads must call.
-template <int NT>
-__device__ void find_two_digits(const DigitBins<NT>& d1, const DigitBins<NT>& d2, int K,
-                                unsigned long long* scan_scratch, int* sh) {
-  constexpr int BPT = DigitBins<NT>::BPT;
-  const int top = kBins - BPT * (int)threadIdx.x;
-  int s1 = 0, s2 = 0;
-#pragma unroll
-  for (int k = 0; k < BPT; ++k) {
-    s1 += d1.h[k];
-    s2 += d2.h[k];
-  }
-  if (threadIdx.x == 0) {
-    sh[0] = -1;
-    sh[1] = 0;
-    sh[2] = -1;
-    sh[3] = 0;
-  }
-  unsigned long long tot;
-  const unsigned long long ex = block_exclusive_scan64<NT>(
-      ((unsigned long long)(uint32_t)s1 << 32) | (uint32_t)s2, scan_scratch, &tot);
-  const int e1 = (int)(ex >> 32), e2 = (int)(uint32_t)ex;
-  if (e1 < K && K <= e1 + s1) {
-    int run = e1;
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      if (run + d1.h[k] >= K) {
-        sh[0] = top - 1 - k;
-        sh[1] = run;
-        break;
-      }
-      run += d1.h[k];
-    }
-  }
-  __syncthreads();
-  if (sh[0] >= 0) {
-    const int need = K - sh[1];
-    if (e2 < need && need <= e2 + s2) {
-      int run = e2;
-#pragma unroll
-      for (int k = 0; k < BPT; ++k) {
-        if (run + d2.h[k] >= need) {
-          sh[2] = top - 1 - k;
-          sh[3] = run;
-          break;
-        }
-        run += d2.h[k];
-      }
-    }
-  }
-  __syncthreads();
 }
 
 // The int32 score of a biased key (score_key's inverse; the folded top key

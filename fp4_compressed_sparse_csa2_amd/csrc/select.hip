@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   };
   uint4 va[kSelLd], vb[kSelLd];
   load_round(va, 0);
-  const DigitBins<kSelNT> bins = load_digit_bins<kSelNT>(h1);
+  const DigitBins<kSelNT> bins = load_digit_bins<kSelNT, kHistReps>(h1);
   for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
@@ -232,7 +232,8 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
   }
   if (tid == 0) a.out_count[b] = written;
-  for (int i = tid; i < kBins; i += kSelNT) h1[i] = 0u;     // ready for the next call
+  uint4* h4 = reinterpret_cast<uint4*>(h1);     // the histogram replicas, for the next call
+  for (int i = tid; i < kCtrlHist2 / 4; i += kSelNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------------ filter
@@ -260,9 +261,13 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 #pragma unroll
     for (int i = 0; i < kFiltPer / 4; ++i) sv[i] = src[i];
   }
-  const DigitBins<kBlock> bins = load_digit_bins<kBlock>(ctrl);
+  const DigitBins<kBlock> bins = load_digit_bins<kBlock, kHistReps>(ctrl);
   find_digit_in<kBlock>(bins, a.K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
+  if (chunk == 0 && threadIdx.x == 0) {  // for the final stage (every block finds the same)
+    ctrl[kCtrlTop] = (uint32_t)sh_t1;
+    ctrl[kCtrlTop + 1] = (uint32_t)sh_above1;
+  }
 
   uint32_t key[kFiltPer];
   uint32_t keep = 0;                     // bit e: entry p0 + e is kept
@@ -290,10 +295,10 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ final
-// One block per sequence.  Both digits of the threshold come from the two
-// histograms (one block scan), so every candidate is classified once: above
-// the threshold key tau, equal to it (the first need_ties of those, in entry
-// order, are selected) or below.
+// One block per sequence.  The top digit comes from the filter, the second
+// from its low-digit histogram (one block scan), so every candidate is
+// classified once: above the threshold key tau, equal to it (the first
+// need_ties of those, in entry order, are selected) or below.
 // Direct plan (at most 16 chunks, none with more kept than its wave holds):
 // wave w requests the first 64*SPL slots of chunk w (SPL = 8 or 16 per lane,
 // chosen by the host from the expected share of K per chunk) together with
@@ -309,7 +314,6 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   constexpr int spl = SPL;
   __shared__ int offs[kMaxSelChunks + 1];
   __shared__ uint2 list[kListCap];
-  __shared__ unsigned long long scan64[kSelWaves];
   __shared__ int scan_scratch[kSelWaves];
   __shared__ int2 wave_tot[kSelWaves];
   __shared__ int sh[6];
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if constexpr (KT::kThree)                      // visible after find_two_digits' barriers
+  if constexpr (KT::kThree)                      // visible after find_digit_in's barriers
     for (int i = tid; i < kBins; i += kSelNT) hist3[i] = 0u;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   uint32_t* h2 = h1 + kCtrlHist2;
@@ -348,9 +352,15 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     }
     my_count = lane < n_chunks ? (int)counts[lane] : 0;
   }
-  const DigitBins<kSelNT> bins1 = load_digit_bins<kSelNT>(h1);
+  // the top digit and the count above it as the filter found them, then the
+  // second digit from the filter's histogram
+  const int top_t1 = (int)h1[kCtrlTop], top_above1 = (int)h1[kCtrlTop + 1];
   const DigitBins<kSelNT> bins2 = load_digit_bins<kSelNT>(h2);
-  find_two_digits<kSelNT>(bins1, bins2, K, scan64, sh);
+  if (tid == 0) {                                // visible after find_digit_in's barriers
+    sh[0] = top_t1;
+    sh[1] = top_above1;
+  }
+  find_digit_in<kSelNT>(bins2, top_t1 >= 0 ? K - top_above1 : 1, scan_scratch, &sh[2], &sh[3]);
   // both digits exist whenever the histograms hold the sequence's n > K
   // entries; if they do not (a workspace that was not zeroed), nothing is
   // selected
@@ -482,7 +492,8 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
   }
   if (tid == 0) a.out_count[b] = written;
-  for (int i = tid; i < 2 * kBins; i += kSelNT) h1[i] = 0u;   // both histograms, for the next call
+  uint4* h4 = reinterpret_cast<uint4*>(h1);     // every control word, for the next call
+  for (int i = tid; i < kCtrlWords / 4; i += kSelNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------------ host
