@@ -44,6 +44,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -102,13 +103,22 @@ def algorithmic_bytes(B, L, H, D, Di, K, W=128):
     return {"append": B * append, "index_topk": B * topk, "sparse_decode": B * decode}
 
 
+def _code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (the sources
+    hold no string literal that contains a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """Digest of the HIP sources; traffic counters are reused only while it matches."""
+    """Digest of the code of the HIP sources (comments and layout excluded);
+    traffic counters are reused only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_compressed_sparse_csa2_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

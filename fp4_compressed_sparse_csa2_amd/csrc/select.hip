@@ -338,8 +338,8 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   const bool few = n_chunks <= kSelWaves;
 
   // this lane's spl slots of chunk `wave` (slots past the row's end read
-  // entry 0 and are never used), the chunk counts and both histograms,
-  // together
+  // entry 0 and are never used), the chunk counts, the filter's top digit
+  // and the low-digit histogram, together
   uint4 sv[spl / 2];
   int my_count = 0;
   if (few) {
