@@ -651,7 +651,10 @@ def cpu_baseline(S: Setup, seconds: float):
         b = (b + 1) % wl.B
     info = threadpoolctl.threadpool_info()
     threads = max([1] + [int(i.get("num_threads", 1)) for i in info])
+    L = int(S.lens.max())
+    per_query = sum(algorithmic_bytes(1, L, wl.H, wl.D, wl.Di, K).values())
     return {"value": done / timed, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "gbs": done / timed * per_query / 1e9,
             "sample": f"{done} whole decode steps (sequences of {WORKLOAD} in turn), "
                       f"{timed:.1f} s of timed oracle work; numpy float64, BLAS threads {threads}",
             "host_cpus": len(os.sched_getaffinity(0))}
