@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     append_index_topk,
     index_topk,
     index_topk_range,
+    index_topk_range_scaled,
     index_topk_scaled,
     key_scales_for,
     lib,

@@ -78,6 +78,12 @@ def lib() -> ctypes.CDLL:
                                                       _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp,
                                                       _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+            "csa2_index_topk_range_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
+                                                            _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                                            _c_vp, _c_sz, _c_vp]),
+            "csa2_topk_merge_values": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                                      _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                                      _c_vp]),
             "csa2_store_key_scales_e4m3": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                                           _c_vp]),
             "csa2_index_topk_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
@@ -465,29 +471,67 @@ def index_topk_range(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: t
 def topk_merge(idx: torch.Tensor, scores: torch.Tensor, counts: torch.Tensor, K: int,
                ws: Workspace, out_idx: torch.Tensor | None = None,
                out_count: torch.Tensor | None = None, out_sel_scores: torch.Tensor | None = None):
-    """Top-K of shard selections: idx / scores int32 [n, B, K_in] (ascending,
-    disjoint, parts in ascending position order), counts int32 [n, B].
-    Returns (idx [B, K], count [B], scores [B, K])."""
+    """Top-K of shard selections: idx int32 [n, B, K_in] (ascending,
+    disjoint, parts in ascending position order), their scores (int32, or
+    float32 values of the scaled indexer) [n, B, K_in], counts int32 [n, B].
+    Returns (idx [B, K], count [B], scores or values [B, K])."""
     n, B, K_in = idx.shape
     dev = idx.device
+    values = scores.dtype == torch.float32
+    sdt = torch.float32 if values else torch.int32
     _need(idx, "idx", torch.int32, dev, (n, B, K_in))
-    _need(scores, "scores", torch.int32, dev, (n, B, K_in))
+    _need(scores, "scores", sdt, dev, (n, B, K_in))
     _need(counts, "counts", torch.int32, dev, (n, B))
     if out_idx is None:
         out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
     if out_count is None:
         out_count = torch.empty((B,), dtype=torch.int32, device=dev)
     if out_sel_scores is None:
-        out_sel_scores = torch.empty((B, K), dtype=torch.int32, device=dev)
+        out_sel_scores = torch.empty((B, K), dtype=sdt, device=dev)
+    _need(out_sel_scores, "out_sel_scores", sdt, dev, (B, K))
     nbytes = lib().csa2_topk_merge_workspace_size(B, n, K_in, K)
     if nbytes == 0:
         raise Csa2Error(f"topk_merge: unsupported sizes n={n} B={B} K_in={K_in} K={K}")
     w = ws.get(nbytes)
-    _check(lib().csa2_topk_merge(B, n, K_in, idx.data_ptr(), scores.data_ptr(), counts.data_ptr(),
-                                 K, out_idx.data_ptr(), out_count.data_ptr(),
-                                 out_sel_scores.data_ptr(), w.data_ptr(), w.numel(), _stream(dev)),
-           "csa2_topk_merge")
+    fn = lib().csa2_topk_merge_values if values else lib().csa2_topk_merge
+    _check(fn(B, n, K_in, idx.data_ptr(), scores.data_ptr(), counts.data_ptr(), K,
+              out_idx.data_ptr(), out_count.data_ptr(), out_sel_scores.data_ptr(), w.data_ptr(),
+              w.numel(), _stream(dev)),
+           "csa2_topk_merge" + ("_values" if values else ""))
     return out_idx, out_count, out_sel_scores
+
+
+def index_topk_range_scaled(cache: Cache, ctx_len: torch.Tensor, max_ctx: int,
+                            q_idx: torch.Tensor, key_scales: torch.Tensor, K: int, p_begin: int,
+                            p_end: int, ws: Workspace, out_idx: torch.Tensor | None = None,
+                            out_count: torch.Tensor | None = None,
+                            out_sel_values: torch.Tensor | None = None):
+    """Scaled Full-layer selection over candidates p_begin <= p < min(p_end,
+    L-128).  Returns (idx [B, K], count [B], values of the selected [B, K])."""
+    dev, B = cache.device, cache.batch
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(q_idx, "q_idx", torch.int8, dev, (B, cache.idx_dim))
+    _need(key_scales, "key_scales", torch.float32, dev, (cache.pages.shape[0], PAGE_TOKENS))
+    if out_idx is None:
+        out_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_sel_values is None:
+        out_sel_values = torch.empty((B, K), dtype=torch.float32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, dev, (B, K))
+    _need(out_count, "out_count", torch.int32, dev, (B,))
+    _need(out_sel_values, "out_sel_values", torch.float32, dev, (B, K))
+    nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
+    if nbytes == 0:
+        raise Csa2Error(f"index_topk_range_scaled: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
+    w = ws.get(nbytes)
+    _check(lib().csa2_index_topk_range_scaled(ctypes.byref(cache.struct), ctx_len.data_ptr(),
+                                              max_ctx, q_idx.data_ptr(), key_scales.data_ptr(), K,
+                                              p_begin, p_end, out_idx.data_ptr(),
+                                              out_count.data_ptr(), out_sel_values.data_ptr(),
+                                              w.data_ptr(), w.numel(), _stream(dev)),
+           "csa2_index_topk_range_scaled")
+    return out_idx, out_count, out_sel_values
 
 
 def lse_merge(outs: torch.Tensor, lses: torch.Tensor, out: torch.Tensor | None = None,

@@ -201,10 +201,10 @@ size_t csa2_topk_merge_workspace_size(int32_t batch, int32_t n_parts, int32_t K_
   return csa2::topk_merge_ws_bytes(batch, n_parts, K_in, K);
 }
 
-int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
-                    const int32_t* scores, const int32_t* counts, int32_t K, int32_t* out_idx,
-                    int32_t* out_count, int32_t* out_sel_scores, void* ws, size_t ws_bytes,
-                    void* stream) {
+static int topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                      const void* scores, const int32_t* counts, int32_t K, int32_t* out_idx,
+                      int32_t* out_count, void* out_sel_scores, void* ws, size_t ws_bytes,
+                      void* stream, bool values) {
   if (counts == nullptr || out_count == nullptr) return CSA2_E_NULL;
   if (K_in > 0 && (idx == nullptr || scores == nullptr)) return CSA2_E_NULL;
   if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
@@ -213,9 +213,26 @@ int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t*
     return CSA2_E_SHAPE;
   const size_t need = csa2::topk_merge_ws_bytes(batch, n_parts, K_in, K);
   if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
-  return status_of(csa2::run_topk_merge(batch, n_parts, K_in, idx, scores, counts, K, out_idx,
-                                        out_count, out_sel_scores, ws,
-                                        static_cast<hipStream_t>(stream)));
+  return status_of(csa2::run_topk_merge(batch, n_parts, K_in, idx,
+                                        static_cast<const int32_t*>(scores), counts, K, out_idx,
+                                        out_count, static_cast<int32_t*>(out_sel_scores), ws,
+                                        static_cast<hipStream_t>(stream), values));
+}
+
+int csa2_topk_merge(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                    const int32_t* scores, const int32_t* counts, int32_t K, int32_t* out_idx,
+                    int32_t* out_count, int32_t* out_sel_scores, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return topk_merge(batch, n_parts, K_in, idx, scores, counts, K, out_idx, out_count,
+                    out_sel_scores, ws, ws_bytes, stream, false);
+}
+
+int csa2_topk_merge_values(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                           const float* values, const int32_t* counts, int32_t K,
+                           int32_t* out_idx, int32_t* out_count, float* out_sel_values, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return topk_merge(batch, n_parts, K_in, idx, values, counts, K, out_idx, out_count,
+                    out_sel_values, ws, ws_bytes, stream, true);
 }
 
 int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
@@ -246,6 +263,26 @@ int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx, const int32_t* po
   return status_of(csa2::run_reindex(args_of(cache), q_idx, nullptr, pool, pool_count, P, K,
                                      out_idx, out_count, out_scores, ws,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_topk_range_scaled(const csa2_cache* cache, const int32_t* ctx_len,
+                                 int32_t max_ctx, const int8_t* q_idx, const float* key_scales,
+                                 int32_t K, int32_t p_begin, int32_t p_end, int32_t* out_idx,
+                                 int32_t* out_count, float* out_sel_values, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q_idx == nullptr || key_scales == nullptr || out_count == nullptr)
+    return CSA2_E_NULL;
+  if (K > 0 && out_idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK || max_ctx < 0 || max_ctx > kMaxCtx) return CSA2_E_SHAPE;
+  if (p_begin < 0 || p_begin % CSA2_PAGE_TOKENS != 0 || p_end < p_begin) return CSA2_E_SHAPE;
+  const size_t need = csa2::index_topk_ws_bytes(cache->batch, max_ctx, K);
+  if (ws == nullptr || ws_bytes < need) return CSA2_E_WORKSPACE;
+  return status_of(csa2::run_index_topk(args_of(cache), ctx_len, max_ctx, q_idx, key_scales, K,
+                                        p_begin, p_end, out_idx, out_count, nullptr,
+                                        reinterpret_cast<int32_t*>(out_sel_values), ws,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const float* key_scales,

@@ -79,9 +79,11 @@ hipError_t run_store_key_scales(const CacheArgs& c, int n, const void* scale, bo
                                 hipStream_t st);
 
 size_t topk_merge_ws_bytes(int batch, int n_parts, int K_in, int K);
+// values: scores are float32 value bits (scaled indexer) instead of int32 scores
 hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
                           const int32_t* scores, const int32_t* counts, int K, int32_t* out_idx,
-                          int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st);
+                          int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st,
+                          bool values = false);
 
 hipError_t run_lse_merge(int n_parts, int batch, int H, int D, const float* outs,
                          const float* lses, float* out, float* lse, hipStream_t st);

@@ -20,6 +20,9 @@ namespace csa2 {
 // strictly ascending position list with its scores) at its offset in the
 // concatenation of the parts, and add their top digits to the sequence's
 // histogram when a selection will run.  Block (0, b) writes the total.
+// VALUES: the scores are float32 values (scaled indexer), stored as their
+// order keys.
+template <bool VALUES>
 __global__ __launch_bounds__(kBlock) void merge_concat_kernel(
     int n_parts, int K_in, int K, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ scores, const int32_t* __restrict__ counts, int batch,
@@ -46,8 +49,15 @@ __global__ __launch_bounds__(kBlock) void merge_concat_kernel(
   for (int i = threadIdx.x; i < mine; i += kBlock) {
     const int32_t sc = scores[src + i];
     pool[dst + i] = idx[src + i];
-    cat_scores[dst + i] = sc;
-    if (do_hist) atomicAdd(&hist[score_key(sc) >> 11], 1u);
+    if constexpr (VALUES) {
+      const float v = __int_as_float(sc);
+      const uint32_t key = value_key(v == 0.0f ? 0.0f : v);
+      cat_scores[dst + i] = (int32_t)key;
+      if (do_hist) atomicAdd(&hist[key >> FloatKeys::kTopShift], 1u);
+    } else {
+      cat_scores[dst + i] = sc;
+      if (do_hist) atomicAdd(&hist[score_key(sc) >> 11], 1u);
+    }
   }
   if (do_hist) {
     __syncthreads();
@@ -83,7 +93,8 @@ size_t topk_merge_ws_bytes(int batch, int n_parts, int K_in, int /*K*/) {
 
 hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
                           const int32_t* scores, const int32_t* counts, int K, int32_t* out_idx,
-                          int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st) {
+                          int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st,
+                          bool values) {
   const int P = n_parts * K_in;
   const MergeWs w = merge_ws(batch, P);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -92,13 +103,15 @@ hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
   int32_t* cat = reinterpret_cast<int32_t*>(base + w.scores);
   int32_t* pool_count = reinterpret_cast<int32_t*>(base + w.pool_count);
   const int stride = row_stride(P);
-  if (n_parts > 0 && K_in > 0) {
-    hipLaunchKernelGGL(merge_concat_kernel, dim3(n_parts, batch), dim3(kBlock), 0, st, n_parts,
-                       K_in, K, idx, scores, counts, batch, pool, cat, pool_count, stride, ctrl);
-  } else {
-    hipLaunchKernelGGL(merge_concat_kernel, dim3(1, batch), dim3(kBlock), 0, st, 0, 0, K, idx,
+  const bool some = n_parts > 0 && K_in > 0;
+  const dim3 grid(some ? n_parts : 1, batch);
+  const int np = some ? n_parts : 0, kin = some ? K_in : 0;
+  if (values)
+    hipLaunchKernelGGL(merge_concat_kernel<true>, grid, dim3(kBlock), 0, st, np, kin, K, idx,
                        scores, counts, batch, pool, cat, pool_count, stride, ctrl);
-  }
+  else
+    hipLaunchKernelGGL(merge_concat_kernel<false>, grid, dim3(kBlock), 0, st, np, kin, K, idx,
+                       scores, counts, batch, pool, cat, pool_count, stride, ctrl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelectArgs a;
@@ -120,7 +133,7 @@ hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
   a.out_idx = out_idx;
   a.out_count = out_count;
   a.out_sel_scores = out_sel_scores;
-  a.float_keys = 0;
+  a.float_keys = values ? 1 : 0;
   return run_select(a, P, st);
 }
 

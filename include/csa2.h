@@ -392,6 +392,30 @@ int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const floa
                         int32_t* out_idx, int32_t* out_count, float* out_values, void* ws,
                         size_t ws_bytes, void* stream);
 
+/*
+ * Context sharding with scaled keys: the same two steps as
+ * csa2_index_topk_range + csa2_topk_merge, ranked by the values v_p.  The
+ * merge is exact for the same reason (the order is total).
+ *
+ * csa2_index_topk_range_scaled -- csa2_index_topk_scaled over the candidate
+ *   positions p_begin <= p < min(p_end, L - 128); out_sel_values (device
+ *   float [batch][K] or NULL) holds the selected values.  Arguments, limits
+ *   and errors as csa2_index_topk_range.
+ * csa2_topk_merge_values -- csa2_topk_merge of shard lists whose scores are
+ *   the float32 values (device float [n_parts][batch][K_in]); out_sel_values
+ *   device float [batch][K] or NULL.  Limits, workspace and errors as
+ *   csa2_topk_merge.
+ */
+int csa2_index_topk_range_scaled(const csa2_cache* cache, const int32_t* ctx_len,
+                                 int32_t max_ctx, const int8_t* q_idx, const float* key_scales,
+                                 int32_t K, int32_t p_begin, int32_t p_end, int32_t* out_idx,
+                                 int32_t* out_count, float* out_sel_values, void* ws,
+                                 size_t ws_bytes, void* stream);
+int csa2_topk_merge_values(int32_t batch, int32_t n_parts, int32_t K_in, const int32_t* idx,
+                           const float* values, const int32_t* counts, int32_t K,
+                           int32_t* out_idx, int32_t* out_count, float* out_sel_values, void* ws,
+                           size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

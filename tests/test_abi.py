@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -129,3 +129,15 @@ def test_append_index_topk_validates_before_launch(L):
                                     1 << 30, None) == -2
     assert L.csa2_append_index_topk(P(c), 4, 1, None, 1, 1, None, 1, 100, 1, 8, 1, 1, None, 1,
                                     16, None) == -4
+
+
+def test_sharded_scaled_calls_validate_before_launch(L):
+    c = _cache()
+    P = ctypes.pointer
+    # range: null scales, p_begin not page-aligned; merge of values: K > n * K_in
+    assert L.csa2_index_topk_range_scaled(P(c), 1, 100, 1, None, 8, 0, 64, 1, 1, None, 1,
+                                          1 << 30, None) == -1
+    assert L.csa2_index_topk_range_scaled(P(c), 1, 100, 1, 1, 8, 32, 200, 1, 1, None, 1,
+                                          1 << 30, None) == -2
+    assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, 1, 40, 1, 1, None, 1, 1 << 30, None) == -2
+    assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, None, 8, 1, 1, None, 1, 1 << 30, None) == -1

@@ -113,3 +113,45 @@ def test_shards_1m_context():
     wl = gen.WORKLOADS["b1_1m"]
     log("shards b1_1m n=8: building the cache")
     _run(GpuCache(wl, keep_kv=False), 8, wl.K)
+
+
+@pytest.mark.parametrize("n,mode", [(4, "lognormal"), (3, "pow2")])
+def test_scaled_shards_merge_to_the_global_selection(n, mode):
+    """Scaled keys: each range's selection equals the oracle's ranking of
+    that range, and the merge of the shard lists equals the one-device
+    scaled Top-K, values included."""
+    from test_gpu_scaled import _store_scales
+    wl = gen.WORKLOADS["b128_rag"].with_(B=6, L=60000, L_min=2000, D=128, H=16, Di=64)
+    log(f"shard scaled n={n} mode={mode}")
+    gc = GpuCache(wl, keep_kv=False)
+    ks, scales = _store_scales(gc, mode)
+    K = 1500
+    B, max_ctx = wl.B, int(gc.lens.max())
+    q_h = gen.idx_query(wl)
+    q = to_dev(q_h)
+    bounds = _bounds(max_ctx, n)
+    pidx = torch.empty((n, B, K), dtype=torch.int32, device=DEV)
+    pval = torch.empty((n, B, K), dtype=torch.float32, device=DEV)
+    pcnt = torch.empty((n, B), dtype=torch.int32, device=DEV)
+    ws = csa2.Workspace(DEV)
+    for s, (a, e) in enumerate(bounds):
+        csa2.index_topk_range_scaled(gc.cache, gc.ctx, max_ctx, q, ks, K, a, e, ws,
+                                     out_idx=pidx[s], out_count=pcnt[s], out_sel_values=pval[s])
+    midx, mcnt, mval = csa2.topk_merge(pidx, pval, pcnt, K, csa2.Workspace(DEV))
+    torch.cuda.synchronize()
+    pidx, pval, pcnt = to_host(pidx), to_host(pval), to_host(pcnt)
+    midx, mcnt, mval = to_host(midx), to_host(mcnt), to_host(mval)
+    for b in range(B):
+        L = int(gc.lens[b])
+        nc = max(0, L - gen.WINDOW)
+        v = OS.scaled_values(OS.indexer_scores(q_h[b], gc.keys[b][:nc]), scales[b][:nc])
+        for s, (a, e) in enumerate(bounds):
+            pos = np.arange(a, min(e, nc)) if min(e, nc) > a else np.zeros(0, np.int64)
+            c = min(K, pos.size)
+            want = np.sort(pos[OS.rank_order_values(v[pos], pos)[:c]])
+            assert int(pcnt[s, b]) == c, f"shard {s} count b={b}"
+            assert np.array_equal(pidx[s, b, :c], want), f"shard {s} positions b={b}"
+            assert np.array_equal(pval[s, b, :c].view(np.uint32), v[want].view(np.uint32))
+        want, wcnt, wval = OS.topk_values(v, L, K)
+        assert int(mcnt[b]) == wcnt and np.array_equal(midx[b], want), f"merge b={b}"
+        assert np.array_equal(mval[b].view(np.uint32), wval.view(np.uint32)), f"merge values b={b}"
