@@ -27,5 +27,6 @@ from ._lib import (  # noqa: F401
     sparse_decode,
     store_key_scales,
     topk_merge,
+    validate_selection,
     workspace_init,
 )

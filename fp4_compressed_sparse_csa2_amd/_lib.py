@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                                       _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp,
                                                       _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
             "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+            "csa2_validate_selection": (ctypes.c_int, [P, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp,
+                                                       _c_vp]),
             "csa2_index_topk_range_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                                             _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                                             _c_vp, _c_sz, _c_vp]),
@@ -342,6 +344,27 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
                                     _ptr(lse), w.data_ptr(), w.numel(), _stream(dev)),
            "csa2_sparse_decode")
     return out, lse
+
+
+# ------------------------------------------------------------------ validation
+SEL_BAD_LENGTH, SEL_BAD_COUNT, SEL_BAD_POSITION, SEL_BAD_PAGE, SEL_NOT_ASCENDING = 1, 2, 4, 8, 16
+
+
+def validate_selection(cache: Cache, ctx_len: torch.Tensor, idx: torch.Tensor,
+                       idx_count: torch.Tensor) -> torch.Tensor:
+    """Contract-violation bits (SEL_*) of sparse_decode's selection inputs,
+    per sequence: int32 [B] on the GPU, 0 where the inputs are valid."""
+    dev, B = cache.device, cache.batch
+    K = idx.shape[1]
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(idx, "idx", torch.int32, dev, (B, K))
+    _need(idx_count, "idx_count", torch.int32, dev, (B,))
+    flags = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib().csa2_validate_selection(ctypes.byref(cache.struct), ctx_len.data_ptr(),
+                                         idx.data_ptr(), idx_count.data_ptr(), K, flags.data_ptr(),
+                                         _stream(dev)),
+           "csa2_validate_selection")
+    return flags
 
 
 # ------------------------------------------------------------------ key scales

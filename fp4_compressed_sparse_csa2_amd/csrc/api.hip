@@ -235,6 +235,23 @@ int csa2_topk_merge_values(int32_t batch, int32_t n_parts, int32_t K_in, const i
                     out_sel_values, ws, ws_bytes, stream, true);
 }
 
+int csa2_validate_selection(const csa2_cache* cache, const int32_t* ctx_len,
+                            const int32_t* idx, const int32_t* idx_count, int32_t K,
+                            uint32_t* flags, void* stream) {
+  static_assert(csa2::kBadLength == CSA2_SEL_BAD_LENGTH && csa2::kBadCount == CSA2_SEL_BAD_COUNT &&
+                    csa2::kBadPosition == CSA2_SEL_BAD_POSITION &&
+                    csa2::kBadPage == CSA2_SEL_BAD_PAGE &&
+                    csa2::kNotAscending == CSA2_SEL_NOT_ASCENDING,
+                "violation bits");
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || idx_count == nullptr || flags == nullptr) return CSA2_E_NULL;
+  if (K > 0 && idx == nullptr) return CSA2_E_NULL;
+  if (K < 0 || K > kMaxK) return CSA2_E_SHAPE;
+  return status_of(csa2::run_validate_selection(args_of(cache), ctx_len, idx, idx_count, K, flags,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
                    const float* outs, const float* lses, float* out, float* lse, void* stream) {
   if (outs == nullptr || lses == nullptr || out == nullptr) return CSA2_E_NULL;

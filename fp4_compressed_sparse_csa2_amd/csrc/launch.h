@@ -85,6 +85,13 @@ hipError_t run_topk_merge(int batch, int n_parts, int K_in, const int32_t* idx,
                           int32_t* out_count, int32_t* out_sel_scores, void* ws, hipStream_t st,
                           bool values = false);
 
+// Contract-violation bits of csa2_validate_selection (the CSA2_SEL_* values).
+constexpr uint32_t kBadLength = 1u, kBadCount = 2u, kBadPosition = 4u, kBadPage = 8u,
+                   kNotAscending = 16u;
+hipError_t run_validate_selection(const CacheArgs& c, const int32_t* ctx_len, const int32_t* idx,
+                                  const int32_t* idx_count, int K, uint32_t* flags,
+                                  hipStream_t st);
+
 hipError_t run_lse_merge(int n_parts, int batch, int H, int D, const float* outs,
                          const float* lses, float* out, float* lse, hipStream_t st);
 

@@ -254,6 +254,33 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_validate_selection -- a debug-time check of the device-side contract
+ * of csa2_sparse_decode's selection inputs, which the other calls do not
+ * report (they skip offending entries and leave the sequence's results
+ * unspecified).  For each sequence b, flags[b] (device uint32 [batch]) gets
+ * the OR of:
+ *   CSA2_SEL_BAD_LENGTH    ctx_len[b] outside [0, 64 * max_pages_per_seq]
+ *   CSA2_SEL_BAD_COUNT     idx_count[b] outside [0, K]
+ *   CSA2_SEL_BAD_POSITION  a counted index outside [0, L - 128) (the
+ *                          candidates; window positions are not selectable)
+ *   CSA2_SEL_BAD_PAGE      a counted index whose page-table entry is outside
+ *                          [0, num_pages) (legal for a context shard's view)
+ *   CSA2_SEL_NOT_ASCENDING the counted indices are not strictly ascending
+ *                          (csa2_sparse_decode accepts any order of distinct
+ *                          positions; in ascending order distinctness is
+ *                          checked, in any other order it is not)
+ * 0 means the inputs meet the contract.  Errors: CSA2_E_NULL, CSA2_E_SHAPE.
+ */
+#define CSA2_SEL_BAD_LENGTH 1u
+#define CSA2_SEL_BAD_COUNT 2u
+#define CSA2_SEL_BAD_POSITION 4u
+#define CSA2_SEL_BAD_PAGE 8u
+#define CSA2_SEL_NOT_ASCENDING 16u
+int csa2_validate_selection(const csa2_cache* cache, const int32_t* ctx_len,
+                            const int32_t* idx, const int32_t* idx_count, int32_t K,
+                            uint32_t* flags, void* stream);
+
+/*
  * Context sharding of long sequences (several devices each holding a
  * contiguous range of a sequence's pages).  Each shard selects among its own
  * candidates under the Full layer's order; csa2_topk_merge turns the shard

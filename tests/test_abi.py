@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -141,3 +141,11 @@ def test_sharded_scaled_calls_validate_before_launch(L):
                                           1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, 1, 40, 1, 1, None, 1, 1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, None, 8, 1, 1, None, 1, 1 << 30, None) == -1
+
+
+def test_validate_selection_validates_before_launch(L):
+    c = _cache()
+    P = ctypes.pointer
+    assert L.csa2_validate_selection(P(c), 1, 1, 1, 8, None, None) == -1      # no flags buffer
+    assert L.csa2_validate_selection(P(c), 1, None, 1, 8, 1, None) == -1      # no indices
+    assert L.csa2_validate_selection(P(c), 1, 1, 1, -1, 1, None) == -2
