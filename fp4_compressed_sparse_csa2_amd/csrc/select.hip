@@ -464,11 +464,39 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     }
     if (tid == 0) offs[n_chunks] = total;
     __syncthreads();
-    // each wave walks whole chunks, its lanes over consecutive candidates
-    for (int c = wave; c < n_chunks; c += kSelWaves) {
-      const int o = offs[c], cnt = offs[c + 1] - o;
-      for (int i = lane; i < cnt && o + i < kListCap; i += 64)
-        list[o + i] = cand_row[(size_t)c * kFiltChunk + i];
+    if (n_chunks <= 2 * kSelWaves) {
+      // few chunks: each wave walks whole chunks, its lanes over consecutive
+      // candidates
+      for (int c = wave; c < n_chunks; c += kSelWaves) {
+        const int o = offs[c], cnt = offs[c + 1] - o;
+        for (int i = lane; i < cnt && o + i < kListCap; i += 64)
+          list[o + i] = cand_row[(size_t)c * kFiltChunk + i];
+      }
+    } else {
+      // many small chunks: list slot f (< kListCap) comes from the chunk c
+      // with offs[c] <= f < offs[c + 1], found by a fixed 12-step bisection
+      // over the offsets (unrolled, so a thread's searches interleave); its
+      // slots are independent, so their loads are in flight together
+      // instead of one chunk after another
+      constexpr int kPer = (kListCap + kSelNT - 1) / kSelNT;
+      const int lim = total < kListCap ? total : kListCap;
+      uint2 v[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int f = tid + q * kSelNT;
+        int c = 0;                                  // offs[0] = 0 <= f
+#pragma unroll
+        for (int step = kMaxSelChunks / 2; step > 0; step >>= 1) {
+          const int cand = c + step;                // at most kMaxSelChunks - 1
+          c = (cand < n_chunks && offs[cand] <= f) ? cand : c;
+        }
+        v[q] = f < lim ? cand_row[(size_t)c * kFiltChunk + (f - offs[c])] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int f = tid + q * kSelNT;
+        if (f < lim) list[f] = v[q];
+      }
     }
     __syncthreads();
     // entry f of the concatenated slot lists (already in entry order)
