@@ -300,9 +300,9 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 // classified once: above the threshold key tau, equal to it (the first
 // need_ties of those, in entry order, are selected) or below.
 // Direct plan (at most 16 chunks, none with more kept than its wave holds):
-// wave w requests the first 64*SPL slots of chunk w (SPL = 8 or 16 per lane,
-// chosen by the host from the expected share of K per chunk) together with
-// the counts and histograms, before any of them is known, and places its
+// wave w requests the first 64*SPL slots of chunk w (SPL = 8, 12 or 16 per
+// lane, chosen by the host from the expected share of K per chunk) together
+// with the counts and the histogram, before any of them is known, and places its
 // chunk's picks from registers after one barrier.  Otherwise the slot lists
 // are concatenated in LDS (the overflow read from the lists themselves) and
 // emitted in order.
@@ -535,13 +535,16 @@ static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStrea
   hipLaunchKernelGGL(select_filter_kernel<KT>, dim3(chunks, a.batch), dim3(kBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 16 candidates per lane in the direct plan when a chunk is expected to
-  // keep more than ~400 (K's share of a chunk, with 25% to spare)
-  const bool wide = (long long)a.K * kFiltChunk * 5 > (long long)max_entries * 4 * 8 * 64;
-  if (wide)
-    hipLaunchKernelGGL((select_final_kernel<16, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
-  else
+  // candidate slots per lane in the direct plan: K's expected share of a
+  // chunk, with 25% to spare, against 64 lanes x SPL
+  const long long share = (long long)a.K * kFiltChunk * 5;       // x 4 * max_entries
+  const long long unit = (long long)max_entries * 4 * 64;
+  if (share <= unit * 8)
     hipLaunchKernelGGL((select_final_kernel<8, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+  else if (share <= unit * 12)
+    hipLaunchKernelGGL((select_final_kernel<12, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+  else
+    hipLaunchKernelGGL((select_final_kernel<16, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   return hipGetLastError();
 }
 
