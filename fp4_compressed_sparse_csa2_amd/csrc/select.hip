@@ -300,8 +300,8 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 // classified once: above the threshold key tau, equal to it (the first
 // need_ties of those, in entry order, are selected) or below.
 // Direct plan (at most 16 chunks, none with more kept than its wave holds):
-// wave w requests the first 64*SPL slots of chunk w (SPL = 8, 12 or 16 per
-// lane, chosen by the host from the expected share of K per chunk) together
+// wave w requests the first 64*SPL slots of chunk w (SPL = 4, 8, 12 or 16
+// per lane, chosen by the host from the expected share of K per chunk) together
 // with the counts and the histogram, before any of them is known, and places its
 // chunk's picks from registers after one barrier.  Otherwise the slot lists
 // are concatenated in LDS (the overflow read from the lists themselves) and
@@ -539,7 +539,9 @@ static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStrea
   // chunk, with 25% to spare, against 64 lanes x SPL
   const long long share = (long long)a.K * kFiltChunk * 5;       // x 4 * max_entries
   const long long unit = (long long)max_entries * 4 * 64;
-  if (share <= unit * 8)
+  if (share <= unit * 4)
+    hipLaunchKernelGGL((select_final_kernel<4, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+  else if (share <= unit * 8)
     hipLaunchKernelGGL((select_final_kernel<8, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   else if (share <= unit * 12)
     hipLaunchKernelGGL((select_final_kernel<12, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
