@@ -361,6 +361,13 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     sh[1] = top_above1;
   }
   find_digit_in<kSelNT>(bins2, top_t1 >= 0 ? K - top_above1 : 1, scan_scratch, &sh[2], &sh[3]);
+  {
+    // every control word has been read (the top digit into registers, the
+    // histogram before find_digit_in's barriers): zero them for the next
+    // call now, while the candidates are classified
+    uint4* h4 = reinterpret_cast<uint4*>(h1);
+    for (int i = tid; i < kCtrlWords / 4; i += kSelNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   // both digits exist whenever the histograms hold the sequence's n > K
   // entries; if they do not (a workspace that was not zeroed), nothing is
   // selected
@@ -520,8 +527,6 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
   }
   if (tid == 0) a.out_count[b] = written;
-  uint4* h4 = reinterpret_cast<uint4*>(h1);     // every control word, for the next call
-  for (int i = tid; i < kCtrlWords / 4; i += kSelNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------------ host
