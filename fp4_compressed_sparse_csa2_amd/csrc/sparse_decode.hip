@@ -28,7 +28,8 @@
 //      straight from those registers (the contraction visits the channels in
 //      the order the lanes hold them, the same for the queries); tile max per
 //      head through LDS;
-//   3. online softmax in the exp2 domain, P (f16) to LDS;
+//   3. online softmax in the exp2 domain against a reference maximum that
+//      moves only when a weight would exceed 2^8, P (f16) to LDS;
 //   4. wave w accumulates O[16 heads][D/4 slice] += P X with MFMA, the X
 //      operand read token-major from the LDS tile by ds_read_b64_tr_b16.
 // A split writes (m, l, unnormalised O); a combine kernel merges the splits
@@ -59,6 +60,7 @@ constexpr int kWinTiles = kWindow / kTile; // window tiles per sequence
 constexpr int kMaxSplits = 64;
 constexpr int kPtCache = 2048;             // page-table entries cached in LDS (131072 positions)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;              // softmax reference moves past this (log2 units)
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -367,12 +369,18 @@ __global__ __launch_bounds__(kBlock, 2) void sparse_decode_kernel(
     if (lg == 0) red_max[lc][wave] = lmax;
     __syncthreads();                    // also: the whole X tile is written
 
-    // online softmax of head lc
+    // online softmax of head lc with a lazily moved reference: the weights
+    // are exp2(s - m_ref), and m_ref moves (rescaling l and O) only when a
+    // tile's maximum exceeds it by more than kLazy, so the weights stay below
+    // 2^kLazy (f16 holds them to the same relative precision) and the
+    // rescale of the accumulators is rare.  All waves take the same decision
+    // from the same maxima.
     const float4 rm = *reinterpret_cast<const float4*>(&red_max[lc][0]);
     const float mt = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
-    const float m_new = fmaxf(m_q, mt);
+    const bool first = m_q == -INFINITY;                 // l and O are still zero
+    const float m_new = (first || mt > m_q + kLazy) ? mt : m_q;
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m_q - m_use);
+    const float alpha = first ? 1.0f : exp2f(m_q - m_use);
     float psum = 0.f;
     half4 ph;
 #pragma unroll

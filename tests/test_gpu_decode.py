@@ -87,9 +87,33 @@ def test_sharp_softmax(q_std, mult):
 
 @pytest.mark.parametrize("B", [1, 3, 64])
 def test_d512_h64_split_plans(B):
-    """B=1: many splits merged by the combine kernel; B=64: one split."""
+    """B=1: many splits merged by the combine kernel; B=3: a few; B=64: one
+    block per (sequence, 16 heads)."""
     wl = gen.WORKLOADS["b8_64k"].with_(B=B, L=4096 + 128 + 37)
     log(f"decode D=512 H=64 B={B}")
+    _decode_and_check(GpuCache(wl), 2048)
+
+
+@pytest.mark.parametrize("B,H,D,K,lmin,lmax,paged", [
+    (64, 64, 512, 256, 0, 700, True),      # ragged, L < 128, counts below K, empty contexts
+    (64, 128, 512, 512, 900, 1500, False),  # eight head groups per sequence
+    (96, 64, 256, 300, 200, 1200, True),    # K not a multiple of the tile
+    (64, 64, 128, 1024, 1100, 1400, False), # K >= candidates for some sequences
+])
+def test_large_batch_ragged(B, H, D, K, lmin, lmax, paged):
+    """Large batches take one block per (sequence, 16 heads) over all of a
+    sequence's tiles: ragged and paged contexts, empty and window-only ones,
+    counts below K."""
+    wl = gen.WORKLOADS["tiny"].with_(B=B, H=H, D=D, Di=64, L=lmax, L_min=lmin, ragged=True,
+                                     paged=paged)
+    log(f"decode large batch B={B} H={H} D={D} K={K} L in [{lmin}, {lmax}] paged={paged}")
+    _decode_and_check(GpuCache(wl), K)
+
+
+@pytest.mark.parametrize("q_std,mult", [(1.0, 1.0), (1.0, 4.0)])
+def test_large_batch_sharp(q_std, mult):
+    wl = gen.WORKLOADS["b8_64k"].with_(B=64, L=3000, q_std=q_std, sigma_mult=mult)
+    log(f"decode large batch sharp q_std={q_std} sigma x{mult}")
     _decode_and_check(GpuCache(wl), 2048)
 
 
