@@ -325,6 +325,46 @@ def chain_calls(S: Setup) -> dict:
             "reindex_gbs": rbytes / (t["reindex_8192_to_2048"] * 1e-6) / 1e9}
 
 
+def ragged_calls(reps: int = 10) -> dict:
+    """The 128-sequence ragged workload (contexts U{8192..131072}, 64-token
+    pages through one global random permutation, every sequence appending one
+    token per step): the step as its three calls, each call's time and rate.
+    Its 3.5 GB cache is far larger than the 256 MB last-level cache, so one
+    replica suffices.  The decode call moves 118 MB here, enough to price it
+    against the HBM roofline on its own."""
+    S = Setup(1, "b128_rag")
+    torch, wl = S.torch, S.wl
+    S.step_unfused(0)
+    torch.cuda.synchronize()
+    calls = {name: time_call(S, fn, 1, reps=reps) for name, fn in (
+        ("append", S.append), ("index_topk", S.index_topk), ("sparse_decode", S.decode),
+        ("step", S.step_unfused))}
+    nb = {"append": 0, "index_topk": 0, "sparse_decode": 0}
+    for L in S.lens:
+        for k, v in algorithmic_bytes(1, int(L), wl.H, wl.D, wl.Di, wl.K).items():
+            nb[k] += v
+    step_bytes = sum(nb.values())
+    dec_flops = 4 * wl.H * wl.D * (wl.K + 128) * wl.B
+    gbs = {k: nb[k] / (calls[k] * 1e-6) / 1e9 for k in nb}
+    res = {"workload": "b128_rag: batch 128, ctx U{8192..131072} (total "
+                       f"{int(S.lens.sum())} tokens), 64-token pages in a permuted page table, "
+                       "64 heads, latent 512 FP4, indexer dim 128, Top-K 2048, SWA 128; step = "
+                       "quantize_append of one token per sequence + index_topk + sparse_decode",
+           "calls_us": calls,
+           "queries_per_s": wl.B / (calls["step"] * 1e-6),
+           "step_bytes": step_bytes,
+           "step_gbs": step_bytes / (calls["step"] * 1e-6) / 1e9,
+           "calls_bytes": nb,
+           "calls_gbs": gbs,
+           "sparse_decode_hbm_frac": gbs["sparse_decode"] / HBM_PEAK_GBS,
+           "sparse_decode_mfma_frac": dec_flops / (calls["sparse_decode"] * 1e-6) / 1e12
+                                      / MFMA_F16_PEAK_TFLOPS,
+           "index_topk_hbm_frac": gbs["index_topk"] / HBM_PEAK_GBS}
+    del S
+    torch.cuda.empty_cache()
+    return res
+
+
 def scaled_calls(S: Setup) -> dict:
     """The scaled indexer (a fp32 key scale per token, ranked by
     fl32(s * score)) at the step's shape: the Full layer's Top-K 2048 and a
@@ -767,11 +807,13 @@ def main() -> int:
     S = Setup(args.replicas)
     wl = S.wl
     wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
-    chain = scaled = None
+    chain = scaled = ragged = None
     if not args.no_extras:
         chain = chain_calls(S)
         chain["schedule"] = schedule_calls(S)
         scaled = scaled_calls(S)
+        log("b128_rag: building the ragged paged cache")
+        ragged = ragged_calls()
     copy_rate = copy_gbs(torch)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
@@ -820,6 +862,7 @@ def main() -> int:
         "copy_reference_gbs": copy_rate,
         "chain": chain,
         "scaled_indexer": scaled,
+        "ragged_b128": ragged,
         "roofline": {"kernel": "csa2_append_index_topk ("
                                + ", ".join(STEP_KERNELS["append_index_topk"]) + ")",
                      "bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
