@@ -79,6 +79,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the chain, schedule and scaled-indexer timings (profiling runs: "
                          "only the step's kernels and their per-call timings are launched)")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="run only the 128-sequence ragged paged workload and print its JSON")
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: three 1 GiB device copies (the counter "
                          "calibration), then --warmup + --steps eager steps; no timing")
@@ -801,6 +803,9 @@ def main() -> int:
         return 2
     if args.counter_run:
         return counter_run(args)
+    if args.ragged_only:
+        print(json.dumps(ragged_calls()), flush=True)
+        return 0
     if args.dcp:
         print(json.dumps(dcp_bench(args)), flush=True)
         return 0
