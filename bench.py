@@ -36,6 +36,13 @@ against the HBM roofline.
 the same seeded workload: whole decode steps of the 8 sequences, repeated
 until about --cpu-seconds of CPU time.
 
+Extra legs in the same line (skipped with --no-extras): the three-layer
+chain's Reindex / Reuse calls and a 20-layer schedule on this cache, the
+scaled indexer, and the 128-sequence ragged paged workload (contexts
+U{8192..131072}, one appended token per sequence per step), where the decode
+call moves enough bytes to be priced against the HBM roofline on its own
+(``--ragged-only`` runs that leg alone).
+
 Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
