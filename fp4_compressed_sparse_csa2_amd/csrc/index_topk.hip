@@ -82,29 +82,33 @@ __device__ __forceinline__ void score_block(const ScoreArgs& sa, int chunk, int 
   int32_t* __restrict__ out_scores = sa.out_scores;
   uint32_t* __restrict__ ctrl = sa.ctrl;
 
-  const int n = seq_candidates(sa.ctx_len, b, max_ctx, max_pages, p_begin, sa.p_end);
   const int chunk0 = chunk * kChunk;
-  if (chunk0 >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave's pages: a wave-uniform index, so the page-table reads are
+  // scalar loads.  They go out together with the sequence's length, before
+  // it is known which of the pages hold candidates (an index past the
+  // table's end reads its last entry and is dropped below).
+  const int lp0 = chunk0 / kPage + __builtin_amdgcn_readfirstlane(wave) * kPagesPerWave;
+  const int lp_last = max_pages - 1 - p_begin / kPage;   // last entry of the table's row
+  const int32_t* pt = page_table + (size_t)b * max_pages + p_begin / kPage;
+  int ptv[kPagesPerWave];
+  if (lp_last >= 0) {
+#pragma unroll
+    for (int pi = 0; pi < kPagesPerWave; ++pi) ptv[pi] = pt[min(lp0 + pi, lp_last)];
+  }
+  const int n = seq_candidates(sa.ctx_len, b, max_ctx, max_pages, p_begin, sa.p_end);
+  if (chunk0 >= n) return;               // n > 0 implies lp_last >= 0
   const bool do_hist = K > 0 && n > K;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
   __builtin_amdgcn_sched_barrier(0);     // the query goes out before the keys
-  const int32_t* pt = page_table + (size_t)b * max_pages + p_begin / kPage;
   int32_t* sc_row = scores + (size_t)b * row_stride(max_ctx);
   int32_t* user_row = out_scores ? out_scores + (size_t)b * max_ctx : nullptr;
   // after the lane-group sums, lane l keeps the score of page row ppos
   const int ppos = PPL * (lane % LPP) + lane / LPP;
-
-  // the wave's pages: a wave-uniform index, so the page-table reads are
-  // scalar loads that all go out before any key load waits on them
-  const int lp0 = chunk0 / kPage + __builtin_amdgcn_readfirstlane(wave) * kPagesPerWave;
   int pg[kPagesPerWave];
 #pragma unroll
-  for (int pi = 0; pi < kPagesPerWave; ++pi) {
-    const int lp = lp0 + pi;
-    pg[pi] = (lp * kPage < n) ? pt[lp] : -1;
-  }
+  for (int pi = 0; pi < kPagesPerWave; ++pi) pg[pi] = ((lp0 + pi) * kPage < n) ? ptv[pi] : -1;
   // then every key load, unconditionally (a page that is not live reads
   // page 0, which always exists, and is skipped), so that page pi's compute
   // waits only for its own loads.  The keys are read once per call:
