@@ -34,7 +34,10 @@ against the HBM roofline.
 
 ``cpu_baseline`` times the plain CPU oracle (the checker, not the product) on
 the same seeded workload: whole decode steps of the 8 sequences, repeated
-until about --cpu-seconds of CPU time.
+until about --cpu-seconds of CPU time.  This leg is the only part of the
+benchmark that runs the oracle; it also checks the GPU step's eager result
+(every sequence: indices bit-exact, outputs within 2e-3) and the scaled
+indexer's selection of sequence 0, and fills ``parity`` from them.
 
 Extra legs in the same line (skipped with --no-extras): the three-layer
 chain's Reindex / Reuse calls and a 20-layer schedule on this cache, the
@@ -377,10 +380,9 @@ def ragged_calls(reps: int = 10) -> dict:
 def scaled_calls(S: Setup) -> dict:
     """The scaled indexer (a fp32 key scale per token, ranked by
     fl32(s * score)) at the step's shape: the Full layer's Top-K 2048 and a
-    Reindex 8192 -> 2048 over a scaled pool, with sequence 0 of the Full
-    layer checked against the oracle."""
-    from oracle import select as OS
-
+    Reindex 8192 -> 2048 over a scaled pool.  Returns the record and the
+    Full layer's selection of sequence 0 with its key scales, which the
+    CPU-oracle leg checks."""
     torch, csa2, gen = S.torch, S.csa2, S.gen
     wl, dev, R = S.wl, S.dev, len(S.caches)
     B, K, Kf = wl.B, wl.K, gen.WORKLOADS["chain_64k"].K
@@ -413,11 +415,7 @@ def scaled_calls(S: Setup) -> dict:
 
     topk(0)
     torch.cuda.synchronize()
-    L0 = int(S.lens[0])
-    v = OS.scaled_values(OS.indexer_scores(S.q_idx_h[0], S.keys[0][:L0 - 128]), host[0][:L0 - 128])
-    want, wc, _ = OS.topk_values(v, L0, K)
-    ok = int(cnt[0]) == wc and np.array_equal(idx[0].cpu().numpy(), want)
-    assert ok, "scaled Top-K differs from the oracle, b=0"
+    check = (idx[0].cpu().numpy(), int(cnt[0]), host[0])
     full_pool(0)
     reindex(0)
     torch.cuda.synchronize()
@@ -429,36 +427,11 @@ def scaled_calls(S: Setup) -> dict:
     L = int(S.lens.max())
     nbytes = algorithmic_bytes(B, L, wl.H, wl.D, wl.Di, K)["index_topk"] + B * 4 * (L - 128)
     return {"key_scales": "fp32 per token, exp(N(0,1))/128",
-            "parity": "sequence 0: Top-K bit-exact",
+            "parity": "skipped (checked in the CPU-oracle leg)",
             "calls_us": {"index_topk_scaled_2048": t_topk, "index_topk_scaled_8192": t_full,
                          "reindex_scaled_8192_to_2048": t_re},
             "index_topk_scaled_bytes": nbytes,
-            "index_topk_scaled_gbs": nbytes / (t_topk * 1e-6) / 1e9}
-
-
-def parity_check(S: Setup) -> str:
-    """Sequences 0 and B-1 of the eager result against the oracle: indices
-    bit-exact, outputs and LSE within 2e-3."""
-    from oracle import attention as OA
-    from oracle import formats as OF
-    from oracle import select as OS
-
-    idx, cnt = S.idx.cpu().numpy(), S.cnt.cpu().numpy()
-    out, lse = S.out.cpu().numpy(), S.lse.cpu().numpy()
-    wl = S.wl
-    worst = 0.0
-    for b in (0, wl.B - 1):
-        L = int(S.lens[b])
-        sc = OS.indexer_scores(S.q_idx_h[b], S.keys[b][:L - 128])
-        want, wc = OS.topk(sc, L, wl.K)
-        assert int(cnt[b]) == wc and np.array_equal(idx[b], want), f"Top-K differs, b={b}"
-        sel = want[:wc]
-        codes, scales = OF.quantize_rows(S.gen.kv_bf16(wl, b, L)[sel])
-        o, l = OA.sparse_decode(S.q_h[b], S.sigma, codes, scales, S.ring_host[b], sel, L)
-        err = max(float(np.max(np.abs(out[b] - o))), float(np.max(np.abs(lse[b] - l))))
-        assert err <= 2e-3, f"attention error {err:.3e}, b={b}"
-        worst = max(worst, err)
-    return f"ok (sequences 0 and {wl.B - 1}: Top-K bit-exact, max-abs error {worst:.1e})"
+            "index_topk_scaled_gbs": nbytes / (t_topk * 1e-6) / 1e9}, check
 
 
 def gpu_bench(args, S: Setup):
@@ -468,8 +441,6 @@ def gpu_bench(args, S: Setup):
         S.step(r)
     torch.cuda.synchronize()
     ref = [t.clone() for t in (S.idx, S.cnt, S.out, S.lse)]
-    parity = "skipped" if args.no_parity else parity_check(S)
-    log(f"parity: {parity}")
 
     per = max(1, 20 // R)                    # replicas x per steps in one graph
     big = capture(S, S.step, [r for _ in range(per) for r in range(R)])
@@ -531,7 +502,7 @@ def gpu_bench(args, S: Setup):
               "p90": float(np.percentile(per_step, 90)), "warm_one_replica": warm_us,
               "replays": len(per_step), "steps_per_replay": S_big,
               "window_restore_us": restore_us}
-    return wall, ev_ms, calls, parity, spread
+    return wall, ev_ms, calls, spread, [t.cpu().numpy() for t in ref]
 
 
 def schedule_calls(S: Setup, n_layers: int = 20) -> dict:
@@ -667,10 +638,27 @@ def dcp_bench(args) -> dict:
 
 
 # ------------------------------------------------------------------ CPU oracle
-def cpu_baseline(S: Setup, seconds: float):
+def scaled_parity(S: Setup, check) -> str:
+    """The scaled indexer's Top-K of sequence 0 (from scaled_calls) against
+    the oracle's ranking of fl32(s * score)."""
+    from oracle import select as OS
+
+    got, got_cnt, scales = check
+    L0 = int(S.lens[0])
+    v = OS.scaled_values(OS.indexer_scores(S.q_idx_h[0], S.keys[0][:L0 - 128]), scales[:L0 - 128])
+    want, wc, _ = OS.topk_values(v, L0, S.wl.K)
+    assert got_cnt == wc and np.array_equal(got, want), "scaled Top-K differs from the oracle, b=0"
+    return "ok (sequence 0 against the oracle: Top-K bit-exact)"
+
+
+def cpu_baseline(S: Setup, seconds: float, gpu=None):
     """The oracle's decode step (append of the new token, indexer scores,
     Top-K, dequantisation of the selected rows, merged attention) on the same
-    seeded sequences, repeated until ``seconds`` of timed work."""
+    seeded sequences, repeated until ``seconds`` of timed work.  Every
+    sequence runs at least once; with ``gpu`` (host copies of the GPU step's
+    idx, count, out, lse) the first run of each sequence is also compared
+    with it, outside the timed parts: indices bit-exact, outputs and LSE
+    within 2e-3.  Returns (baseline record, parity string)."""
     import threadpoolctl
 
     from oracle import attention as OA
@@ -680,6 +668,7 @@ def cpu_baseline(S: Setup, seconds: float):
     wl = S.wl
     K = wl.K
     stored = {}                       # the oracle cache's rows at each sequence's selection
+    worst, checked = 0.0, set()
     done, timed = 0, 0.0
     b = 0
     while timed < seconds or done < wl.B:
@@ -693,20 +682,30 @@ def cpu_baseline(S: Setup, seconds: float):
         if b not in stored:           # cache content (written at prefill), not part of the step
             stored[b] = OF.quantize_rows(S.gen.kv_bf16(wl, b, L)[sel])
         t2 = time.perf_counter()
-        OA.sparse_decode(S.q_h[b], S.sigma, *stored[b], S.ring_host[b], sel, L)
+        o, lse = OA.sparse_decode(S.q_h[b], S.sigma, *stored[b], S.ring_host[b], sel, L)
         t3 = time.perf_counter()
         timed += (t1 - t0) + (t3 - t2)
+        if gpu is not None and b not in checked:
+            g_idx, g_cnt, g_out, g_lse = (t[b] for t in gpu)
+            assert int(g_cnt) == c and np.array_equal(g_idx, idx), f"Top-K differs, b={b}"
+            err = max(float(np.max(np.abs(g_out - o))), float(np.max(np.abs(g_lse - lse))))
+            assert err <= 2e-3, f"attention error {err:.3e}, b={b}"
+            worst = max(worst, err)
+            checked.add(b)
         done += 1
         b = (b + 1) % wl.B
     info = threadpoolctl.threadpool_info()
     threads = max([1] + [int(i.get("num_threads", 1)) for i in info])
     L = int(S.lens.max())
     per_query = sum(algorithmic_bytes(1, L, wl.H, wl.D, wl.Di, K).values())
+    parity = ("skipped" if gpu is None else
+              f"ok (all {wl.B} sequences against the oracle: Top-K bit-exact, "
+              f"max-abs error {worst:.1e})")
     return {"value": done / timed, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "gbs": done / timed * per_query / 1e9,
             "sample": f"{done} whole decode steps (sequences of {WORKLOAD} in turn), "
                       f"{timed:.1f} s of timed oracle work; numpy float64, BLAS threads {threads}",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0))}, parity
 
 
 # ------------------------------------------------------------------ counters
@@ -818,12 +817,12 @@ def main() -> int:
         return 0
     S = Setup(args.replicas)
     wl = S.wl
-    wall, ev_ms, calls, parity, spread = gpu_bench(args, S)
-    chain = scaled = ragged = None
+    wall, ev_ms, calls, spread, eager = gpu_bench(args, S)
+    chain = scaled = ragged = scaled_check = None
     if not args.no_extras:
         chain = chain_calls(S)
         chain["schedule"] = schedule_calls(S)
-        scaled = scaled_calls(S)
+        scaled, scaled_check = scaled_calls(S)
         log("b128_rag: building the ragged paged cache")
         ragged = ragged_calls()
     copy_rate = copy_gbs(torch)
@@ -881,11 +880,15 @@ def main() -> int:
                      "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "frac_of_copy_reference": fused_gbs / copy_rate,
                      "launch_us": calls["append_index_topk"], "bytes_per_launch": fused_bytes},
-        "parity": parity,
+        "parity": "skipped (checked in the CPU-oracle leg)",
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(S, args.cpu_seconds)
+        log("timing the CPU oracle (and checking the GPU step against it)")
+        res["cpu_baseline"], res["parity"] = cpu_baseline(
+            S, args.cpu_seconds, None if args.no_parity else eager)
+        log(f"parity: {res['parity']}")
+        if scaled is not None and not args.no_parity:
+            scaled["parity"] = scaled_parity(S, scaled_check)
     print(json.dumps(res), flush=True)
     return 0
 
