@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "csa2_store_key_scales": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
             "csa2_validate_selection": (ctypes.c_int, [P, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp,
                                                        _c_vp]),
+            "csa2_validate_window": (ctypes.c_int, [P, _c_vp, _c_vp, _c_vp, _c_vp]),
             "csa2_index_topk_range_scaled": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                                             _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                                             _c_vp, _c_sz, _c_vp]),
@@ -175,16 +176,27 @@ class Cache:
 
 
 class Workspace:
-    """A zero-initialised workspace that grows on demand (one per call kind)."""
+    """A zero-initialised workspace that grows on demand.
+
+    The library keeps per-sequence control words at the start of a workspace
+    and returns them to zero at the end of every call, but where the scratch
+    that follows them begins depends on the call's batch and kind.  So the
+    buffer is zeroed again whenever it is handed to a call of another kind
+    (Full-layer selection, Reindex, Top-K merge, decode) or another batch
+    size, and whenever it grows."""
 
     def __init__(self, device):
         self.device = torch.device(device)
         self.buf = None
+        self.key = None
 
-    def get(self, nbytes: int) -> torch.Tensor:
+    def get(self, nbytes: int, kind: str = "", batch: int = 0) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
             workspace_init(self.buf)
+        elif self.key != (kind, batch):
+            workspace_init(self.buf)
+        self.key = (kind, batch)
         return self.buf
 
 
@@ -231,7 +243,7 @@ def index_topk(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.T
     nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
     if nbytes == 0:
         raise Csa2Error(f"index_topk: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "topk", B)
     _check(lib().csa2_index_topk(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
                                  q_idx.data_ptr(), K, out_idx.data_ptr(), out_count.data_ptr(),
                                  _ptr(out_scores), w.data_ptr(), w.numel(), _stream(dev)),
@@ -270,7 +282,7 @@ def append_index_topk(cache: Cache, x: torch.Tensor, seq: torch.Tensor, pos: tor
     nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
     if nbytes == 0:
         raise Csa2Error(f"append_index_topk: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "topk", B)
     _check(lib().csa2_append_index_topk(ctypes.byref(cache.struct), n, x.data_ptr(), _ptr(keys),
                                         seq.data_ptr(), pos.data_ptr(), _ptr(swa),
                                         ctx_len.data_ptr(), max_ctx, q_idx.data_ptr(), K,
@@ -300,7 +312,7 @@ def reindex(cache: Cache, q_idx: torch.Tensor, pool: torch.Tensor, pool_count: t
     nbytes = lib().csa2_reindex_workspace_size(B, P, K)
     if nbytes == 0:
         raise Csa2Error(f"reindex: unsupported sizes B={B} P={P} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "reindex", B)
     _check(lib().csa2_reindex(ctypes.byref(cache.struct), q_idx.data_ptr(), pool.data_ptr(),
                               pool_count.data_ptr(), P, K, out_idx.data_ptr(),
                               out_count.data_ptr(), _ptr(out_scores), w.data_ptr(), w.numel(),
@@ -337,7 +349,7 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
     nbytes = lib().csa2_sparse_decode_workspace_size(B, H, D, K)
     if nbytes == 0:
         raise Csa2Error(f"sparse_decode: unsupported sizes B={B} H={H} D={D} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "decode", B)
     _check(lib().csa2_sparse_decode(ctypes.byref(cache.struct), ctx_len.data_ptr(), H,
                                     q.data_ptr(), float(softmax_scale), idx.data_ptr(),
                                     idx_count.data_ptr(), K, _ptr(swa), out.data_ptr(),
@@ -364,6 +376,23 @@ def validate_selection(cache: Cache, ctx_len: torch.Tensor, idx: torch.Tensor,
                                          idx.data_ptr(), idx_count.data_ptr(), K, flags.data_ptr(),
                                          _stream(dev)),
            "csa2_validate_selection")
+    return flags
+
+
+WIN_NOT_F16, WIN_NOT_FINITE = 1, 2
+
+
+def validate_window(cache: Cache, ctx_len: torch.Tensor, swa: torch.Tensor) -> torch.Tensor:
+    """Window-ring check bits (WIN_*) per sequence: int32 [B] on the GPU, 0
+    where every live slot is finite and exact in fp16."""
+    dev, B = cache.device, cache.batch
+    swa = _as_u16(swa)
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(swa, "swa", torch.uint16, dev, (B, WINDOW, cache.head_dim))
+    flags = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib().csa2_validate_window(ctypes.byref(cache.struct), ctx_len.data_ptr(),
+                                      swa.data_ptr(), flags.data_ptr(), _stream(dev)),
+           "csa2_validate_window")
     return flags
 
 
@@ -416,7 +445,7 @@ def index_topk_scaled(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: 
     nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
     if nbytes == 0:
         raise Csa2Error(f"index_topk_scaled: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "topk", B)
     _check(lib().csa2_index_topk_scaled(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
                                         q_idx.data_ptr(), key_scales.data_ptr(), K,
                                         out_idx.data_ptr(), out_count.data_ptr(),
@@ -449,7 +478,7 @@ def reindex_scaled(cache: Cache, q_idx: torch.Tensor, key_scales: torch.Tensor,
     nbytes = lib().csa2_reindex_workspace_size(B, P, K)
     if nbytes == 0:
         raise Csa2Error(f"reindex_scaled: unsupported sizes B={B} P={P} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "reindex", B)
     _check(lib().csa2_reindex_scaled(ctypes.byref(cache.struct), q_idx.data_ptr(),
                                      key_scales.data_ptr(), pool.data_ptr(),
                                      pool_count.data_ptr(), P, K, out_idx.data_ptr(),
@@ -482,7 +511,7 @@ def index_topk_range(cache: Cache, ctx_len: torch.Tensor, max_ctx: int, q_idx: t
     nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
     if nbytes == 0:
         raise Csa2Error(f"index_topk_range: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "topk", B)
     _check(lib().csa2_index_topk_range(ctypes.byref(cache.struct), ctx_len.data_ptr(), max_ctx,
                                        q_idx.data_ptr(), K, p_begin, p_end, out_idx.data_ptr(),
                                        out_count.data_ptr(), out_sel_scores.data_ptr(),
@@ -515,7 +544,7 @@ def topk_merge(idx: torch.Tensor, scores: torch.Tensor, counts: torch.Tensor, K:
     nbytes = lib().csa2_topk_merge_workspace_size(B, n, K_in, K)
     if nbytes == 0:
         raise Csa2Error(f"topk_merge: unsupported sizes n={n} B={B} K_in={K_in} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "merge", B)
     fn = lib().csa2_topk_merge_values if values else lib().csa2_topk_merge
     _check(fn(B, n, K_in, idx.data_ptr(), scores.data_ptr(), counts.data_ptr(), K,
               out_idx.data_ptr(), out_count.data_ptr(), out_sel_scores.data_ptr(), w.data_ptr(),
@@ -547,7 +576,7 @@ def index_topk_range_scaled(cache: Cache, ctx_len: torch.Tensor, max_ctx: int,
     nbytes = lib().csa2_index_topk_workspace_size(B, max_ctx, K)
     if nbytes == 0:
         raise Csa2Error(f"index_topk_range_scaled: unsupported sizes B={B} max_ctx={max_ctx} K={K}")
-    w = ws.get(nbytes)
+    w = ws.get(nbytes, "topk", B)
     _check(lib().csa2_index_topk_range_scaled(ctypes.byref(cache.struct), ctx_len.data_ptr(),
                                               max_ctx, q_idx.data_ptr(), key_scales.data_ptr(), K,
                                               p_begin, p_end, out_idx.data_ptr(),

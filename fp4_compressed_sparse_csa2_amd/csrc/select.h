@@ -21,9 +21,11 @@ namespace csa2 {
 // atomics on the busiest bins over two addresses), the low-digit histogram
 // of the entries whose top digit is the threshold's (kBins words, filled by
 // the multi-block filter), the top digit and the count above it as the
-// filter found them (two words), then spare words.  The size does not depend
-// on the call's sizes, so a zeroed workspace stays zeroed between calls of
-// any shape.
+// filter found them (two words), then spare words.  Sequence b's words sit
+// at b * kCtrlWords from the start of the workspace whatever the call's
+// sizes, and every call returns them to zero; the scratch that follows them
+// starts after batch * kCtrlWords words, so a workspace handed to a call
+// with another batch must be zeroed again first.
 constexpr int kHistReps = 2;
 constexpr int kCtrlHist2 = kHistReps * kBins;
 constexpr int kCtrlTop = kCtrlHist2 + kBins;

@@ -121,3 +121,18 @@ def test_deterministic_and_workspace_reuse():
     for x, y in ((a, b), (a, c)):
         assert all(np.array_equal(u, v) for u, v in zip(x, y))
     _check(gc, q, 300, ws=ws)
+
+
+def test_workspace_shared_across_batch_sizes():
+    """One Workspace object for calls of different batch sizes: batch 1 on
+    the multi-block plan (150K candidates), then batch 2 with a smaller
+    max_ctx, then batch 1 again.  The control words of the batch-2 call sit
+    where the batch-1 call's chunk counts and scores were, so the binding
+    zeroes the buffer again when the batch changes; every call bit-exact."""
+    big = gen.WORKLOADS["tiny"].with_(L=150_000, Di=64)
+    small = gen.WORKLOADS["tiny"].with_(B=2, L=9000, Di=64)
+    log("topk workspace shared: B=1 L=150000, B=2 L=9000, B=1 again")
+    g1, g2 = GpuCache(big, keep_kv=False), GpuCache(small, keep_kv=False)
+    ws = csa2.Workspace(DEV)
+    for gc in (g1, g2, g1, g2):
+        _check(gc, gen.idx_query(gc.wl), 2048, ws=ws)
