@@ -69,6 +69,18 @@ def rows_of(pages: np.ndarray, page_table: np.ndarray, D: int, Di: int,
     return pages[pg[:, None], ci], pages[pg[:, None], si]
 
 
+def row_byte_index(page_table: np.ndarray, D: int, Di: int, b: int,
+                   pos: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Flat byte indices, into the pages array seen as one byte vector, of the
+    codes [n, D/2] and scales [n, D/16] of positions ``pos`` of sequence b."""
+    s_off, _ = _offsets(D, Di)
+    pos = np.asarray(pos, dtype=np.int64)
+    base = page_table[b, pos // PAGE].astype(np.int64)[:, None] * page_bytes(D, Di)
+    r = (pos % PAGE)[:, None]
+    return (base + r * (D // 2) + np.arange(D // 2)[None, :],
+            base + s_off + r * (D // 16) + np.arange(D // 16)[None, :])
+
+
 def keys_of(pages: np.ndarray, page_table: np.ndarray, D: int, Di: int,
             b: int, pos: np.ndarray) -> np.ndarray:
     """Stored int8 indexer keys [n, Di] of positions ``pos`` of sequence b."""

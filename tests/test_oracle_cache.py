@@ -25,3 +25,17 @@ def test_append_roundtrip_paged():
     assert np.array_equal(C.keys_of(pages, pt, D, Di, 0, pos), keys)
     assert np.array_equal(swa[0], gen.swa_ring(wl, kv, 300))
     assert C.page_bytes(512, 128) == 26624 and C.page_bytes(128, 64) == 8704
+
+
+def test_row_byte_index_matches_rows_of():
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=700, paged=True, append_steps=0)
+    lens = gen.ctx_lens(wl)
+    pt, npages = gen.page_table(wl, lens)
+    D, Di = wl.D, wl.Di
+    pages = np.random.default_rng(3).integers(0, 256, (npages, C.page_bytes(D, Di))).astype(np.uint8)
+    pos = np.array([0, 1, 63, 64, 65, 300, 699])
+    for b in range(2):
+        ci, si = C.row_byte_index(pt, D, Di, b, pos)
+        codes, scales = C.rows_of(pages, pt, D, Di, b, pos)
+        flat = pages.reshape(-1)
+        assert np.array_equal(flat[ci], codes) and np.array_equal(flat[si], scales)

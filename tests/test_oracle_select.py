@@ -109,3 +109,26 @@ def test_reuse_is_identity():
     idx = np.array([3, 9, -1], dtype=np.int32)
     out, c = S.reuse(idx, 2)
     assert c == 2 and np.array_equal(out, idx) and out is not idx
+
+
+def test_reindex_brute_force_shuffled_pools():
+    """Integer Reindex against Python sorted(): a pool chosen by one query,
+    ranked by another; ascending and shuffled pools, junk past the count."""
+    rng = np.random.default_rng(21)
+    for trial in range(6):
+        L = int(rng.integers(200, 700))
+        n = L - 128
+        keys = rng.integers(-4, 5, (L, 8)).astype(np.int8)        # small range: many ties
+        q_own, q_pool = (rng.integers(-127, 128, 8).astype(np.int8) for _ in range(2))
+        sc = S.indexer_scores(q_own, keys)
+        brute = _brute_scores(q_own, keys)
+        pool, count = S.topk(S.indexer_scores(q_pool, keys[:n]), L, int(rng.integers(1, n)))
+        shuffled = pool.copy()
+        shuffled[:count] = rng.permutation(pool[:count])
+        shuffled[count:] = rng.integers(0, n, pool.size - count)
+        for pl in (pool, shuffled):
+            for K in (0, 1, count // 3, count, count + 5):
+                got, c = S.reindex(pl, count, sc[np.maximum(pl, 0)], K)
+                ranked = sorted((int(p) for p in pl[:count]), key=lambda p: (-brute[p], p))
+                want = sorted(ranked[:K])
+                assert c == len(want) and list(got) == want + [-1] * (K - len(want))
