@@ -28,5 +28,6 @@ from ._lib import (  # noqa: F401
     store_key_scales,
     topk_merge,
     validate_selection,
+    validate_window,
     workspace_init,
 )

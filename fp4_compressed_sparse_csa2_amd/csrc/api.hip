@@ -252,6 +252,17 @@ int csa2_validate_selection(const csa2_cache* cache, const int32_t* ctx_len,
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int csa2_validate_window(const csa2_cache* cache, const int32_t* ctx_len, const uint16_t* swa,
+                         uint32_t* flags, void* stream) {
+  static_assert(csa2::kWinNotF16 == CSA2_WIN_NOT_F16 && csa2::kWinNotFinite == CSA2_WIN_NOT_FINITE,
+                "window bits");
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || swa == nullptr || flags == nullptr) return CSA2_E_NULL;
+  return status_of(csa2::run_validate_window(args_of(cache), ctx_len, swa, flags,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int csa2_lse_merge(int32_t n_parts, int32_t batch, int32_t H, int32_t head_dim,
                    const float* outs, const float* lses, float* out, float* lse, void* stream) {
   if (outs == nullptr || lses == nullptr || out == nullptr) return CSA2_E_NULL;

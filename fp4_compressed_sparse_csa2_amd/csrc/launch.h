@@ -92,6 +92,11 @@ hipError_t run_validate_selection(const CacheArgs& c, const int32_t* ctx_len, co
                                   const int32_t* idx_count, int K, uint32_t* flags,
                                   hipStream_t st);
 
+// Window-ring check bits of csa2_validate_window (the CSA2_WIN_* values).
+constexpr uint32_t kWinNotF16 = 1u, kWinNotFinite = 2u;
+hipError_t run_validate_window(const CacheArgs& c, const int32_t* ctx_len, const uint16_t* swa,
+                               uint32_t* flags, hipStream_t st);
+
 hipError_t run_lse_merge(int n_parts, int batch, int H, int D, const float* outs,
                          const float* lses, float* out, float* lse, hipStream_t st);
 

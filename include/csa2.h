@@ -40,13 +40,16 @@
  *   entries without touching memory outside the buffers, and results for
  *   the affected sequence are unspecified.
  * - Workspaces: calls that need scratch take (ws, ws_bytes), sized by the
- *   matching *_workspace_size query.  A workspace must be zero-filled once
- *   before its first use (csa2_workspace_init, or any zeroing allocation);
- *   every call returns the control words it uses to zero before it
- *   finishes, so later calls on the same stream need no re-initialisation.
- *   One workspace serves one kind of call at a time: two calls in flight on
- *   different streams need two workspaces, and a workspace handed from one
- *   kind of call to another must be re-initialised.
+ *   matching *_workspace_size query.  A workspace starts with per-sequence
+ *   control words (batch of them) that must be zero when a call starts;
+ *   the scratch after them is laid out from the call's batch and sizes.
+ *   So a workspace must be zero-filled (csa2_workspace_init, or any zeroing
+ *   allocation) before its first use, and again whenever it is handed to a
+ *   call of another kind or with another `batch` than the call before it.
+ *   Every call returns its control words to zero before it finishes, so
+ *   later calls of the same kind and batch on the same stream need no
+ *   re-initialisation, whatever their other sizes.  Two calls in flight on
+ *   different streams need two workspaces.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -233,10 +236,12 @@ int csa2_reindex(const csa2_cache* cache, const int8_t* q_idx,
  *              16 <= H <= 128.
  * idx          device int32 [batch][K]: c distinct positions in [0, L-128);
  *              entries at or beyond the count are ignored.  0 <= K <= 65536.
- * swa          device uint16 [batch][128][D] bf16 ring of this layer; its
- *              values must be finite with magnitude <= 65504 (the window rows
- *              run through fp16 MFMA operands; magnitudes below 2^-14 keep
- *              fp16 subnormal precision).  NULL: no window rows (a context
+ * swa          device uint16 [batch][128][D] bf16 ring of this layer.  The
+ *              window rows run through fp16 MFMA operands, so its live values
+ *              must be finite and exactly representable in fp16: magnitude at
+ *              most 65504, and a multiple of 2^-24 below 2^-14 (bf16 values
+ *              from 2^-14 to 65280 always are).  csa2_validate_window reports
+ *              rings outside this range.  NULL: no window rows (a context
  *              shard that holds none of the last 128 positions, see below).
  * out          device float [batch][H][D]; lse device float [batch][H] or NULL.
  * ws           workspace of csa2_sparse_decode_workspace_size(batch, H, D, K).
@@ -279,6 +284,26 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
 int csa2_validate_selection(const csa2_cache* cache, const int32_t* ctx_len,
                             const int32_t* idx, const int32_t* idx_count, int32_t K,
                             uint32_t* flags, void* stream);
+
+/*
+ * csa2_validate_window -- a debug-time check of the window-ring contract of
+ * csa2_sparse_decode (the ring's values are bf16 in the method; the decode
+ * holds them as exact fp16 operands).  For each sequence b, flags[b] (device
+ * uint32 [batch]) gets the OR, over the live slots of swa[b] (those of
+ * positions [max(0, L - 128), L), L = ctx_len[b] clamped to the page table), of:
+ *   CSA2_WIN_NOT_F16     a finite value that fp16 does not hold exactly
+ *                        (magnitude above 65504, or too fine below 2^-14);
+ *                        csa2_sparse_decode would round it
+ *   CSA2_WIN_NOT_FINITE  an infinite or NaN value
+ * Dead slots (L < 128) are not read.  Errors: CSA2_E_NULL, CSA2_E_SHAPE,
+ * CSA2_E_UNSUPPORTED.
+ * Source of the window: zulogic "DeepSeek V4 1-Flash 架构拆解", section 4;
+ * infernews.com V4.1 Flash page, section 2.
+ */
+#define CSA2_WIN_NOT_F16 1u
+#define CSA2_WIN_NOT_FINITE 2u
+int csa2_validate_window(const csa2_cache* cache, const int32_t* ctx_len, const uint16_t* swa,
+                         uint32_t* flags, void* stream);
 
 /*
  * Context sharding of long sequences (several devices each holding a

@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -141,6 +141,14 @@ def test_sharded_scaled_calls_validate_before_launch(L):
                                           1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, 1, 40, 1, 1, None, 1, 1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, None, 8, 1, 1, None, 1, 1 << 30, None) == -1
+
+
+def test_validate_window_validates_before_launch(L):
+    c = _cache()
+    P = ctypes.byref
+    assert L.csa2_validate_window(P(c), 1, 1, None, None) == -1          # no flags buffer
+    assert L.csa2_validate_window(P(c), 1, None, 1, None) == -1          # no ring
+    assert L.csa2_validate_window(P(_cache(D=384)), 1, 1, 1, None) == -3
 
 
 def test_validate_selection_validates_before_launch(L):

@@ -71,6 +71,53 @@ def test_codec_sweep_bit_exact(D, Di):
     assert np.array_equal(got, want)
 
 
+def _every_amax_rows(D: int) -> np.ndarray:
+    """One 16-channel group per finite non-negative bf16 value as its group
+    maximum (all 32,640 of them, +0 included): the maximum sits at a rotating
+    channel, the other 15 channels are random bf16 values of magnitude at most
+    the maximum, both signs, a third of them at an E2M1 midpoint times amax/6
+    (next to the element rounding boundaries).  So the scale rounding of amax/6 is driven through the
+    kernel for every amax it can see, not only at the centre of each scale
+    code's interval."""
+    allb = np.arange(1 << 15, dtype=np.uint32).astype(np.uint16)        # sign bit clear
+    allb = allb[((allb >> 7) & 0xFF) != 0xFF]                           # finite: 32,640 values
+    assert allb.size == 32640
+    amax = OF.bf16_value(allb)
+    rng = np.random.default_rng(32640)
+    u = rng.uniform(-1.0, 1.0, (allb.size, 15))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])            # E2M1 midpoints / 6
+    tie = rng.random((allb.size, 15)) < 1.0 / 3.0
+    u = np.where(tie, rng.choice(mids, (allb.size, 15)) * np.sign(u) / 6.0, u)
+    vals = (u * amax[:, None]).astype(np.float32)
+    bits = gen.f32_to_bf16_bits(vals)
+    over = np.abs(OF.bf16_value(bits)) > amax[:, None]                   # rounded past the max
+    bits = np.where(over, allb[:, None] | (bits & np.uint16(0x8000)), bits)
+    g = np.empty((allb.size, 16), np.uint16)
+    for j in range(16):
+        sel = np.arange(allb.size) % 16 == j
+        g[sel, :j], g[sel, j], g[sel, j + 1:] = bits[sel, :j], allb[sel], bits[sel, j:]
+    assert np.all(np.max(np.abs(OF.bf16_value(g)), axis=1) == amax)
+    per_row = D // 16
+    n_rows = -(-g.shape[0] // per_row)
+    return np.resize(g, (n_rows * per_row, 16)).reshape(n_rows, D)
+
+
+@pytest.mark.parametrize("D,Di", [(512, 128), (128, 64)])
+def test_every_bf16_amax_bit_exact(D, Di):
+    x = _every_amax_rows(D)
+    n = x.shape[0]
+    log(f"quantize every-amax D={D}: {n} rows, 32640 groups")
+    mp = -(-n // 64)
+    pt = np.arange(mp, dtype=np.int32)[None, :]
+    cache = csa2.Cache.allocate(1, mp, mp, D, Di, torch.from_numpy(pt), DEV)
+    csa2.quantize_append(cache, to_dev(x), torch.zeros(n, dtype=torch.int32, device=DEV),
+                         torch.arange(n, dtype=torch.int32, device=DEV))
+    got = to_host(cache.pages)
+    want = np.zeros_like(got)
+    OC.append(want, pt, D, Di, np.zeros(n, int), np.arange(n), x, None, None)
+    assert np.array_equal(got, want)
+
+
 def test_window_ring_and_paged_append():
     wl = gen.WORKLOADS["tiny"].with_(B=3, L=500, paged=True, append_steps=0)
     lens = np.array([500, 130, 70], np.int32)

@@ -40,3 +40,52 @@ def test_planted_violations():
     view = csa2.Cache(gc.cache.pages, to_dev(pt), wl.D, wl.Di)
     flags = to_host(csa2.validate_selection(view, gc.ctx, idx, cnt))
     assert flags[6] == _lib.SEL_BAD_PAGE and not np.delete(flags, 6).any()
+
+
+def test_window_ring_range():
+    """csa2_validate_window flags a live window value that fp16 does not hold
+    exactly (above 65504, or too fine below 2^-14) and non-finite values, not
+    dead slots; rings at the edge of the range (65280, 2^-24, 2^-14 - 2^-24
+    steps) pass and decode within the bar against the oracle."""
+    from gpu_common import ATOL, assert_close, oracle_decode, oracle_topk
+    wl = gen.WORKLOADS["tiny"].with_(B=6, L=1000)
+    log("validate window ring range")
+    gc = GpuCache(wl)
+    lens = gc.lens.astype(np.int32).copy()
+    lens[5] = 50                                      # slots >= 50 are dead
+    ring = gc.rings[0].copy()
+    bf = lambda v: gen.f32_to_bf16_bits(np.array([v], np.float32))[0]
+    edge = [bf(65280.0), bf(-65280.0), bf(2.0 ** -24), bf(-(2.0 ** -14)), bf(3 * 2.0 ** -24)]
+    ring[0, 7, :len(edge)] = edge                     # exact in fp16: no flag
+    ring[1, 3, 5] = bf(70000.0)                       # above 65504
+    ring[2, 100, 9] = bf(1e-6)                        # below 2^-14, not a multiple of 2^-24
+    ring[3, 0, 0] = 0x7F80                            # +inf
+    ring[4, 1, 1] = 0x7FC1                            # NaN
+    ring[5, 60, 0] = 0x7FC1                           # a dead slot: not read
+    flags = to_host(csa2.validate_window(gc.cache, to_dev(lens), to_dev(ring)))
+    want = np.array([0, _lib.WIN_NOT_F16, _lib.WIN_NOT_F16, _lib.WIN_NOT_FINITE,
+                     _lib.WIN_NOT_FINITE, 0])
+    assert np.array_equal(flags, want), flags
+
+    # the edge values decode within the bar.  The query is scaled by 2^-12 so
+    # that one window value of 65280 does not take the whole softmax (then
+    # outputs stay near 200, where fp32 rounding is far below the bar).
+    edge_ring = gc.rings[0].copy()
+    edge_ring[:, 7, :len(edge)] = edge
+    q = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(gen.query(wl)) * np.float32(2.0 ** -12))
+    qi = gen.idx_query(wl)
+    sigma = float(gen.softmax_scale(wl))
+    idx, cnt = csa2.index_topk(gc.cache, gc.ctx, int(gc.lens.max()), to_dev(qi), wl.K,
+                               csa2.Workspace(DEV))
+    out, lse = csa2.sparse_decode(gc.cache, gc.ctx, to_dev(q), sigma, idx, cnt, to_dev(edge_ring),
+                                  csa2.Workspace(DEV))
+    assert not to_host(csa2.validate_window(gc.cache, gc.ctx, to_dev(edge_ring))).any()
+    idx_h, cnt_h, out_h, lse_h = map(to_host, (idx, cnt, out, lse))
+    for b in range(wl.B):
+        L = int(gc.lens[b])
+        _, want, wcnt = oracle_topk(gc.keys[b], qi[b], L, wl.K)
+        assert int(cnt_h[b]) == wcnt and np.array_equal(idx_h[b], want)
+        sel = want[:wcnt]
+        o, l = oracle_decode(q[b], sigma, gc.kv_rows(b, sel), edge_ring[b], sel, L)
+        assert_close(out_h[b], o, ATOL, f"edge ring out b={b}")
+        assert_close(lse_h[b], l, ATOL, f"edge ring lse b={b}")
