@@ -53,7 +53,12 @@ def test_window_ring_range():
     gc = GpuCache(wl)
     lens = gc.lens.astype(np.int32).copy()
     lens[5] = 50                                      # slots >= 50 are dead
-    ring = gc.rings[0].copy()
+    # the N(0,1) draw holds a few values below 2^-14 that fp16 subnormals do
+    # not hold exactly (about one per 16K): zero them, so that only the
+    # planted values decide the flags
+    base = gc.rings[0].copy()
+    base[np.abs(gen.bf16_bits_to_f32(base)) < 2.0 ** -14] = 0
+    ring = base.copy()
     bf = lambda v: gen.f32_to_bf16_bits(np.array([v], np.float32))[0]
     edge = [bf(65280.0), bf(-65280.0), bf(2.0 ** -24), bf(-(2.0 ** -14)), bf(3 * 2.0 ** -24)]
     ring[0, 7, :len(edge)] = edge                     # exact in fp16: no flag
@@ -70,7 +75,7 @@ def test_window_ring_range():
     # the edge values decode within the bar.  The query is scaled by 2^-12 so
     # that one window value of 65280 does not take the whole softmax (then
     # outputs stay near 200, where fp32 rounding is far below the bar).
-    edge_ring = gc.rings[0].copy()
+    edge_ring = base.copy()
     edge_ring[:, 7, :len(edge)] = edge
     q = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(gen.query(wl)) * np.float32(2.0 ** -12))
     qi = gen.idx_query(wl)
