@@ -62,7 +62,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for p in procs:
         _wait(p)
     tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host stub a compile pass failed to emit
+    # fails the link here instead of the first dlopen
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+            "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

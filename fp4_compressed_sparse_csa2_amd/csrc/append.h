@@ -80,8 +80,9 @@ __device__ __forceinline__ void append_token(const AppendArgs& a, int tok, int l
 
   uint8_t* page = a.pages + (size_t)pg * lay.page_bytes;
   const int r = p % kPage;
-  *reinterpret_cast<uint32_t*>(page + r * (D / 2) + l * 4) = packed;
-  if ((l & 1) == 0) page[lay.scales_off + r * (D / 16) + (l >> 1)] = (uint8_t)sc;
+  uint8_t* row = page + r * lay.row_bytes;
+  *reinterpret_cast<uint32_t*>(row + l * 4) = packed;
+  if ((l & 1) == 0) row[D / 2 + (l >> 1)] = (uint8_t)sc;
   if (a.key != nullptr && l < DI / 16) {
     const uint4 kv = *reinterpret_cast<const uint4*>(a.key + (size_t)tok * DI + l * 16);
     *reinterpret_cast<uint4*>(page + lay.keys_off + r * DI + l * 16) = kv;

@@ -13,14 +13,16 @@ constexpr int kBlock = 256;    // threads per block for every kernel here
 constexpr int kKeyBias = 1 << 21;  // int8 scores at Di <= 128 lie in [-2^21 + 2^14, 2^21]
 constexpr int kBins = 2048;    // radix digit = 11 bits; two digits cover the 22-bit key
 
-// Byte layout of one page: codes [64][D/2], scales [64][D/16], keys [64][Di].
+// Byte layout of one page: 64 rows of R = D/2 + D/16 bytes (a row is its
+// E2M1 codes, D/2 bytes, then its E4M3 scales, D/16 bytes, so one token's
+// FP4 row is one contiguous run), then the 64 int8 key rows of Di bytes.
 struct PageLayout {
-  int scales_off;
-  int keys_off;
-  int page_bytes;
+  int row_bytes;      // R
+  int keys_off;       // 64 * R
+  int page_bytes;     // 64 * (R + Di)
 };
 __host__ __device__ constexpr PageLayout page_layout(int D, int Di) {
-  return PageLayout{kPage * (D / 2), kPage * (D / 2 + D / 16), kPage * (D / 2 + D / 16 + Di)};
+  return PageLayout{D / 2 + D / 16, kPage * (D / 2 + D / 16), kPage * (D / 2 + D / 16 + Di)};
 }
 
 // Radix key of an indexer score: score + 2^21 as a 22-bit unsigned number.

@@ -79,11 +79,15 @@ typedef enum {
  *
  * pages       device, num_pages * csa2_page_bytes(head_dim, idx_dim) bytes.
  *             Page layout (64 positions each), back to back:
- *               codes  [64][head_dim/2]   E2M1 codes; channel 2j in the low
- *                                         nibble of byte j, 2j+1 in the high
- *               scales [64][head_dim/16]  E4M3 (OCP "FN") scale of channels
- *                                         16g..16g+15 in byte g
- *               keys   [64][idx_dim]      int8 indexer keys
+ *               rows   [64][R], R = head_dim/2 + head_dim/16 bytes, the FP4
+ *                      row of one token, contiguous:
+ *                        codes  [head_dim/2]   E2M1 codes; channel 2j in the
+ *                                              low nibble of byte j, 2j+1 in
+ *                                              the high nibble
+ *                        scales [head_dim/16]  E4M3 (OCP "FN") scale of
+ *                                              channels 16g..16g+15 in byte g
+ *               keys   [64][idx_dim]  int8 indexer keys
+ *             (R = 288 at head_dim 512; a page is 26,624 bytes with idx_dim 128.)
  * page_table  device int32 [batch][max_pages_per_seq]: physical page of
  *             logical page i of sequence b (position p lives in page
  *             page_table[b][p/64], row p%64).  Contiguous caches use the

@@ -6,6 +6,7 @@ oracle-side references computed from those same host draws only.
 """
 from __future__ import annotations
 
+import contextlib
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -106,3 +107,36 @@ def assert_close(got: np.ndarray, want: np.ndarray, atol: float, what: str) -> f
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert err <= atol, f"{what}: max-abs error {err:.3e} > {atol:.1e}"
     return err
+
+
+# Decode plans a test can force through the library's tuning variables:
+# (heads per block, FP4 tiles per split or None for the library's choice).
+DECODE_PLANS = {
+    "auto": (None, None),
+    "hg64": ("64", None),
+    "hg64_split3": ("64", "3"),
+    "hg64_split1": ("64", "1"),
+    "hg16_split2": ("16", "2"),
+}
+
+
+@contextlib.contextmanager
+def decode_plan(name: str):
+    """Run csa2_sparse_decode calls under the named plan (environment
+    variables read by the library on every call), then restore."""
+    hg, tps = DECODE_PLANS[name]
+    keys = {"CSA2_DECODE_HEADS_PER_BLOCK": hg, "CSA2_DECODE_SPLIT_TILES": tps}
+    old = {k: os.environ.get(k) for k in keys}
+    try:
+        for k, v in keys.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v

@@ -72,9 +72,12 @@ def test_window_ring_range():
                      _lib.WIN_NOT_FINITE, 0])
     assert np.array_equal(flags, want), flags
 
-    # the edge values decode within the bar.  The query is scaled by 2^-12 so
-    # that one window value of 65280 does not take the whole softmax (then
-    # outputs stay near 200, where fp32 rounding is far below the bar).
+    # the edge values decode within the bar, taken relative to the output's
+    # magnitude here: the f16 weights that multiply the rows carry a relative
+    # rounding of 2^-12, so a row of magnitude 65280 moves an output by up to
+    # 16 times its weight, against about 1e-3 for the N(0,1) rows the absolute
+    # 2e-3 is set for.  The query is scaled by 2^-12 so that the value 65280
+    # does not take the whole softmax (outputs stay near 200).
     edge_ring = base.copy()
     edge_ring[:, 7, :len(edge)] = edge
     q = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(gen.query(wl)) * np.float32(2.0 ** -12))
@@ -92,5 +95,6 @@ def test_window_ring_range():
         assert int(cnt_h[b]) == wcnt and np.array_equal(idx_h[b], want)
         sel = want[:wcnt]
         o, l = oracle_decode(q[b], sigma, gc.kv_rows(b, sel), edge_ring[b], sel, L)
-        assert_close(out_h[b], o, ATOL, f"edge ring out b={b}")
+        assert_close(out_h[b], o, ATOL * max(1.0, float(np.max(np.abs(o)))),
+                     f"edge ring out b={b}")
         assert_close(lse_h[b], l, ATOL, f"edge ring lse b={b}")
