@@ -24,7 +24,9 @@ from ._lib import (  # noqa: F401
     reindex,
     reindex_scaled,
     restore_window,
+    NOALLOC_SCRATCH_BYTES,
     sparse_decode,
+    sparse_decode_noalloc,
     store_key_scales,
     topk_merge,
     validate_selection,

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 PAGE_TOKENS = 64
 WINDOW = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20       # fixed scratch of sparse_decode_noalloc, per device
 
 _c_i32 = ctypes.c_int32
 _c_vp = ctypes.c_void_p
@@ -66,6 +67,9 @@ def lib() -> ctypes.CDLL:
             "csa2_sparse_decode": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, ctypes.c_float, _c_vp,
                                                   _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
                                                   _c_vp]),
+            "csa2_sparse_decode_noalloc": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, ctypes.c_float,
+                                                          _c_vp, _c_vp, _c_i32, _c_vp, _c_vp,
+                                                          _c_vp, _c_vp]),
             "csa2_index_topk_range": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
                                                      _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
                                                      _c_vp]),
@@ -321,13 +325,7 @@ def reindex(cache: Cache, q_idx: torch.Tensor, pool: torch.Tensor, pool_count: t
     return out_idx, out_count
 
 
-def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_scale: float,
-                  idx: torch.Tensor, idx_count: torch.Tensor, swa: torch.Tensor | None,
-                  ws: Workspace, out: torch.Tensor | None = None,
-                  lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Merged sparse attention.  q bf16 [B, H, D]; idx int32 [B, K]; swa bf16
-    [B, 128, D], or None for no window rows (a context shard without the
-    tail).  Returns (out fp32 [B, H, D], lse fp32 [B, H] or None)."""
+def _decode_args(cache: Cache, ctx_len, q, idx, idx_count, swa, out, lse, want_lse):
     dev, B, D = cache.device, cache.batch, cache.head_dim
     q = _as_u16(q)
     swa = None if swa is None else _as_u16(swa)
@@ -346,6 +344,19 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, dev, (B, H))
+    return q, swa, H, K, out, lse
+
+
+def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_scale: float,
+                  idx: torch.Tensor, idx_count: torch.Tensor, swa: torch.Tensor | None,
+                  ws: Workspace, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Merged sparse attention.  q bf16 [B, H, D]; idx int32 [B, K]; swa bf16
+    [B, 128, D], or None for no window rows (a context shard without the
+    tail).  Returns (out fp32 [B, H, D], lse fp32 [B, H] or None)."""
+    q, swa, H, K, out, lse = _decode_args(cache, ctx_len, q, idx, idx_count, swa, out, lse,
+                                          want_lse)
+    B, D = cache.batch, cache.head_dim
     nbytes = lib().csa2_sparse_decode_workspace_size(B, H, D, K)
     if nbytes == 0:
         raise Csa2Error(f"sparse_decode: unsupported sizes B={B} H={H} D={D} K={K}")
@@ -353,8 +364,25 @@ def sparse_decode(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor, softmax_
     _check(lib().csa2_sparse_decode(ctypes.byref(cache.struct), ctx_len.data_ptr(), H,
                                     q.data_ptr(), float(softmax_scale), idx.data_ptr(),
                                     idx_count.data_ptr(), K, _ptr(swa), out.data_ptr(),
-                                    _ptr(lse), w.data_ptr(), w.numel(), _stream(dev)),
+                                    _ptr(lse), w.data_ptr(), w.numel(), _stream(cache.device)),
            "csa2_sparse_decode")
+    return out, lse
+
+
+def sparse_decode_noalloc(cache: Cache, ctx_len: torch.Tensor, q: torch.Tensor,
+                          softmax_scale: float, idx: torch.Tensor, idx_count: torch.Tensor,
+                          swa: torch.Tensor | None, out: torch.Tensor, lse: torch.Tensor | None):
+    """sparse_decode on the library's fixed per-device scratch: no workspace,
+    and the caller passes the outputs (lse may be None), so the call
+    allocates nothing.  Calls that overlap in time on one device race on the
+    scratch.  Returns (out, lse)."""
+    q, swa, H, K, out, lse = _decode_args(cache, ctx_len, q, idx, idx_count, swa, out, lse,
+                                          False)
+    _check(lib().csa2_sparse_decode_noalloc(ctypes.byref(cache.struct), ctx_len.data_ptr(), H,
+                                            q.data_ptr(), float(softmax_scale), idx.data_ptr(),
+                                            idx_count.data_ptr(), K, _ptr(swa), out.data_ptr(),
+                                            _ptr(lse), _stream(cache.device)),
+           "csa2_sparse_decode_noalloc")
     return out, lse
 
 

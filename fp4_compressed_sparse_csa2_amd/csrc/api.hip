@@ -3,6 +3,9 @@
 // reads of device memory on the host.
 #include "csa2.h"
 
+#include <atomic>
+#include <mutex>
+
 #include "append.h"
 #include "common.h"
 #include "launch.h"
@@ -55,6 +58,38 @@ constexpr int32_t kMaxK = 65536;
 constexpr int32_t kMaxCtx = 1 << 24;
 constexpr int32_t kMaxParts = 64;
 
+// Scratch of csa2_sparse_decode_noalloc: one copy per device, alive until the
+// process ends.  On the host `scratch` names a host-side stand-in, not device
+// memory, so host code only ever passes the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kNoAllocScratch = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, looked up on its first use.
+hipError_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,6 +107,8 @@ const char* csa2_status_string(int status) {
     case CSA2_E_UNSUPPORTED: return "CSA2_E_UNSUPPORTED: head_dim/idx_dim/heads not supported";
     case CSA2_E_WORKSPACE: return "CSA2_E_WORKSPACE: workspace NULL or too small";
     case CSA2_E_HIP: return "CSA2_E_HIP: a kernel launch failed";
+    case CSA2_E_SCRATCH:
+      return "CSA2_E_SCRATCH: the call needs more than the fixed allocation-free scratch";
     default: return "unknown csa2 status";
   }
 }
@@ -353,6 +390,32 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
   return status_of(csa2::run_sparse_decode(args_of(cache), ctx_len, H, q, softmax_scale, idx,
                                            idx_count, K, swa, out, lse, ws,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int csa2_sparse_decode_noalloc(const csa2_cache* cache, const int32_t* ctx_len, int32_t H,
+                               const uint16_t* q, float softmax_scale, const int32_t* idx,
+                               const int32_t* idx_count, int32_t K, const uint16_t* swa,
+                               float* out, float* lse, void* stream) {
+  int st = check_cache(cache);
+  if (st != CSA2_OK) return st;
+  if (ctx_len == nullptr || q == nullptr || idx_count == nullptr || out == nullptr)
+    return CSA2_E_NULL;
+  if (K > 0 && idx == nullptr) return CSA2_E_NULL;
+  if (H < 16 || H > 128 || H % 16 != 0) return CSA2_E_UNSUPPORTED;
+  if (K < 0 || K > kMaxK) return CSA2_E_SHAPE;
+  if (csa2::sparse_decode_ws_bytes(cache->batch, H, cache->head_dim, K) > kNoAllocScratch)
+    return CSA2_E_SCRATCH;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hs != nullptr) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(hs, &sdev) != hipSuccess)
+      return CSA2_E_HIP;
+    if (cur != sdev) return CSA2_E_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return CSA2_E_HIP;
+  return status_of(csa2::run_sparse_decode(args_of(cache), ctx_len, H, q, softmax_scale, idx,
+                                           idx_count, K, swa, out, lse, ws, hs));
 }
 
 }  // extern "C"

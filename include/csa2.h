@@ -29,7 +29,8 @@
  * --------------------------------
  * - Every pointer argument is DEVICE memory unless marked (host).  All
  *   buffers are owned by the caller; the library allocates nothing, frees
- *   nothing and keeps no state between calls.
+ *   nothing and keeps no state between calls, except the fixed per-device
+ *   scratch of csa2_sparse_decode_noalloc.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Every call only enqueues work on it and returns; nothing synchronises.
  * - Return value: CSA2_OK, or a negative csa2_status for a host-side
@@ -71,7 +72,9 @@ typedef enum {
   CSA2_E_SHAPE = -2,         /* a size or count is out of range               */
   CSA2_E_UNSUPPORTED = -3,   /* head_dim / idx_dim / heads not supported      */
   CSA2_E_WORKSPACE = -4,     /* workspace NULL or smaller than required       */
-  CSA2_E_HIP = -5            /* a kernel launch failed                        */
+  CSA2_E_HIP = -5,           /* a kernel launch failed                        */
+  CSA2_E_SCRATCH = -6        /* request needs more than an allocation-free
+                                call's fixed scratch                          */
 } csa2_status;
 
 /*
@@ -261,6 +264,28 @@ int csa2_sparse_decode(const csa2_cache* cache, const int32_t* ctx_len, int32_t 
                        const int32_t* idx, const int32_t* idx_count, int32_t K,
                        const uint16_t* swa, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_sparse_decode_noalloc -- csa2_sparse_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results, limits and errors as csa2_sparse_decode, minus
+ * (ws, ws_bytes); the split partials go to a fixed scratch array the library
+ * holds on each device, CSA2_NOALLOC_SCRATCH_BYTES bytes, for as long as the
+ * process lives.  A call whose csa2_sparse_decode_workspace_size exceeds that
+ * returns CSA2_E_SCRATCH before anything is enqueued.  The call allocates and
+ * frees nothing; its first call on a device looks up that device's scratch
+ * address (once, with the device current).  `stream` must belong to the
+ * current device.  All calls on one device share its scratch, and nothing in
+ * it needs to start at any value (every partial a call reads it wrote
+ * first), but two calls that overlap in time on one device (different
+ * streams, or host threads) race on it: serialise them.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa2_sparse_decode_noalloc(const csa2_cache* cache, const int32_t* ctx_len, int32_t H,
+                               const uint16_t* q, float softmax_scale,
+                               const int32_t* idx, const int32_t* idx_count, int32_t K,
+                               const uint16_t* swa, float* out, float* lse, void* stream);
 
 /*
  * csa2_validate_selection -- a debug-time check of the device-side contract

@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -36,7 +36,7 @@ def test_page_bytes_and_strings(L):
     assert L.csa2_page_bytes(512, 128) == 64 * (256 + 32 + 128)
     assert L.csa2_page_bytes(128, 64) == 64 * (64 + 8 + 64)
     assert L.csa2_page_bytes(100, 64) == 0 and L.csa2_page_bytes(512, 96) == 0
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.csa2_status_string(s).startswith(b"CSA2_")
 
 
@@ -157,3 +157,21 @@ def test_validate_selection_validates_before_launch(L):
     assert L.csa2_validate_selection(P(c), 1, 1, 1, 8, None, None) == -1      # no flags buffer
     assert L.csa2_validate_selection(P(c), 1, None, 1, 8, 1, None) == -1      # no indices
     assert L.csa2_validate_selection(P(c), 1, 1, 1, -1, 1, None) == -2
+
+
+def test_noalloc_decode_validates_before_launch(L):
+    """csa2_sparse_decode_noalloc checks its arguments, and that the request
+    fits the fixed scratch, before it looks up or touches any device."""
+    import fp4_compressed_sparse_csa2_amd as csa2
+    P = ctypes.byref
+    c = _cache()
+    assert L.csa2_sparse_decode_noalloc(P(c), 1, 24, 1, 1.0, 1, 1, 8, 1, 1, None, None) == -3
+    assert L.csa2_sparse_decode_noalloc(P(c), 1, 16, 1, 1.0, 1, 1, 8, 1, None, None, None) == -1
+    assert L.csa2_sparse_decode_noalloc(P(c), 1, 16, 1, 1.0, 1, 1, -1, 1, 1, None, None) == -2
+    # 128 sequences x 128 heads x D = 512 with K = 65536 takes split partials
+    # far beyond the scratch
+    big = _cache(batch=128)
+    assert L.csa2_sparse_decode_workspace_size(128, 128, 512, 65536) > csa2.NOALLOC_SCRATCH_BYTES
+    assert L.csa2_sparse_decode_noalloc(P(big), 1, 128, 1, 1.0, 1, 1, 65536, 1, 1, None,
+                                        None) == -6
+    assert b"SCRATCH" in L.csa2_status_string(-6)
