@@ -27,10 +27,13 @@ Timing.  Inputs are resident in HBM before the timed region.  The caches are
 replicated and the steps rotate over the replicas so that no step finds its
 keys in the 256 MB last-level cache.  Steps are captured in HIP graphs
 (torch.cuda.CUDAGraph) and replayed; the timed region is bracketed by
-torch.cuda.synchronize() and HIP events on the stream the kernels run on.
-A second timed region replays graphs of one library call at a time to give
-each call's average duration; the dominant call (csa2_index_topk) is priced
-against the HBM roofline.
+torch.cuda.synchronize() and HIP events on the stream the kernels run on;
+``value``, ``ms_per_step`` and ``hbm_gbs`` all come from those events (the
+host wall clock is reported beside them).  A second timed region replays
+graphs of one library call at a time to give each call's average duration;
+the dominant call (csa2_append_index_topk) is priced against the HBM
+roofline, and against the library's read-only stream kernel
+(csa2_stream_read over 2 GiB) timed in the same run.
 
 ``cpu_baseline`` times the plain CPU oracle (the checker, not the product) on
 the same seeded workload: whole decode steps of the 8 sequences, repeated
@@ -40,11 +43,14 @@ benchmark that runs the oracle; it also checks the GPU step's eager result
 indexer's selection of sequence 0, and fills ``parity`` from them.
 
 Extra legs in the same line (skipped with --no-extras): the three-layer
-chain's Reindex / Reuse calls and a 20-layer schedule on this cache, the
-scaled indexer, and the 128-sequence ragged paged workload (contexts
-U{8192..131072}, one appended token per sequence per step), where the decode
-call moves enough bytes to be priced against the HBM roofline on its own
-(``--ragged-only`` runs that leg alone).
+chain on this cache (Full Top-K 8192 and its decode over the 8192, Reindex
+to 2048 and its decode, a Reuse decode; each call and the whole chain step)
+and a 20-layer schedule, the scaled indexer, the 128-sequence ragged paged
+workload (contexts U{8192..131072}, one appended token per sequence per
+step), where the decode call moves enough bytes to be priced against the
+HBM roofline on its own (``--ragged-only`` runs that leg alone), and the
+one-sequence 1M-token workload's step with its own roofline figure, checked
+against the oracle in the CPU leg.
 
 Prints one JSON line on stdout; progress goes to stderr.
 
@@ -151,7 +157,7 @@ def measured_traffic(kernel: str):
 
 # ------------------------------------------------------------------ GPU side
 class Setup:
-    def __init__(self, replicas: int, workload: str = WORKLOAD):
+    def __init__(self, replicas: int, workload: str = WORKLOAD, keep_kv: bool = False):
         import torch
 
         import fp4_compressed_sparse_csa2_amd as csa2
@@ -166,7 +172,7 @@ class Setup:
         t0 = time.perf_counter()
         cache = csa2.Cache.allocate(B, pt.shape[1], npages, D, Di, torch.from_numpy(pt), dev)
         ring = np.zeros((B, gen.WINDOW, D), np.uint16)
-        self.keys, self.tail = [], []
+        self.keys, self.tail, self.kv = [], [], []
         x_new = np.empty((B, D), np.uint16)
         k_new = np.empty((B, Di), np.int8)
         for b in range(B):
@@ -178,6 +184,8 @@ class Setup:
             ring[b] = gen.swa_ring(wl, kv, Lb)
             x_new[b], k_new[b] = kv[Lb - 1], keys[Lb - 1]
             self.keys.append(keys)
+            if keep_kv:
+                self.kv.append(kv)
             del kv
         torch.cuda.synchronize()
         log(f"cache built: {npages} pages of {cache.pages.shape[1]} B "
@@ -282,6 +290,26 @@ def copy_gbs(torch, nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / t / 1e9
 
 
+def read_gbs(torch, csa2, nbytes: int = 2 << 30) -> float:
+    """Rate of the library's read-only stream kernel (csa2_stream_read, 16-byte
+    non-temporal loads) over a buffer far larger than the last-level cache:
+    the in-run reference for a read-bound kernel on this HBM."""
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    csa2.stream_read(a, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        csa2.stream_read(a, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 10
+    del a
+    return nbytes / t / 1e9
+
+
 def chain_calls(S: Setup) -> dict:
     """The Reindex / Reuse rows timed on this cache, with the shapes of the
     three-layer chain workload: a Full Top-K pool of 8192, a Reindex layer
@@ -302,9 +330,18 @@ def chain_calls(S: Setup) -> dict:
     ws = [csa2.Workspace(dev) for _ in range(4)]
     sigma = float(gen.softmax_scale(wlc))
 
+    q0 = S.t(gen.query(wlc, 0))
+    out_f = torch.empty((B, wl.H, wl.D), dtype=torch.float32, device=dev)
+    lse_f = torch.empty((B, wl.H), dtype=torch.float32, device=dev)
+    ws_f = csa2.Workspace(dev)
+
     def full(r):
         csa2.index_topk(S.caches[r], S.ctx, S.max_ctx, S.q_idx, Kf, ws[0], out_idx=pool,
                         out_count=pc)
+
+    def dec_full_layer(r):
+        csa2.sparse_decode(S.caches[r], S.ctx, q0, sigma, pool, pc, S.rings[r], ws_f,
+                           out=out_f, lse=lse_f)
 
     def reindex(r):
         csa2.reindex(S.caches[r], q1, pool, pc, K2, ws[1], out_idx=idx2, out_count=c2)
@@ -317,20 +354,38 @@ def chain_calls(S: Setup) -> dict:
         csa2.sparse_decode(S.caches[r], S.ctx, qb, sigma, idx2, c2, S.rings[r], ws[3],
                            out=outs[1], lse=lses[1])
 
-    for r in range(R):                       # eager pass sizes the workspaces
+    def chain_step(r):
+        """The three layers' hot path in order: Full selection and attention,
+        Reindex refilter and attention, Reuse attention."""
         full(r)
+        dec_full_layer(r)
         reindex(r)
         dec_reindex_layer(r)
         dec_reuse_layer(r)
+
+    for r in range(R):                       # eager pass sizes the workspaces
+        chain_step(r)
     torch.cuda.synchronize()
     t = {name: time_call(S, fn, R) for name, fn in (
-        ("full_index_topk_8192", full), ("reindex_8192_to_2048", reindex),
+        ("full_index_topk_8192", full), ("sparse_decode_full_layer_8192", dec_full_layer),
+        ("reindex_8192_to_2048", reindex),
         ("sparse_decode_reindex_layer", dec_reindex_layer),
-        ("sparse_decode_reuse_layer", dec_reuse_layer))}
+        ("sparse_decode_reuse_layer", dec_reuse_layer), ("chain_step", chain_step))}
+    L = S.max_ctx
     rbytes = B * (Kf * (4 + wl.Di) + wl.Di + 4 * K2)
-    return {"workload": "chain_64k shapes on the b8_64k cache: Full Top-K 8192 -> Reindex "
-                        "Top-K 2048 -> decode of the Reindex layer and of a Reuse layer",
+    full_b = algorithmic_bytes(B, L, wl.H, wl.D, wl.Di, Kf)
+    dec2 = algorithmic_bytes(B, L, wl.H, wl.D, wl.Di, K2)["sparse_decode"]
+    step_bytes = full_b["index_topk"] + full_b["sparse_decode"] + rbytes + 2 * dec2
+    return {"workload": "chain_64k on the b8_64k cache: Full layer (Top-K 8192 and its "
+                        "decode over the 8192) -> Reindex layer (Top-K 2048 of the pool and "
+                        "its decode) -> Reuse layer (decode over the Reindex indices)",
             "calls_us": t,
+            "step_us": t["chain_step"],
+            "layer_queries_per_s": 3 * B / (t["chain_step"] * 1e-6),
+            "step_bytes": step_bytes,
+            "step_gbs": step_bytes / (t["chain_step"] * 1e-6) / 1e9,
+            "full_decode_8192_gbs": full_b["sparse_decode"]
+                                    / (t["sparse_decode_full_layer_8192"] * 1e-6) / 1e9,
             "reindex_layer_step_us": t["reindex_8192_to_2048"] + t["sparse_decode_reindex_layer"],
             "reuse_layer_step_us": t["sparse_decode_reuse_layer"],
             "reindex_algorithmic_bytes": rbytes,
@@ -375,6 +430,48 @@ def ragged_calls(reps: int = 10) -> dict:
     del S
     torch.cuda.empty_cache()
     return res
+
+
+def long_context_calls(replicas: int = 3):
+    """The one-sequence workload b1_1m (1,048,576 cached tokens, Top-K 2048,
+    3-sigma boost of 1% of the keys) on one device: the step of the headline
+    (append fused into the Full layer's selection, then attention) and its
+    two calls, timed as graph replays over cold cache replicas (each about
+    436 MB, together past the 256 MB last-level cache).  Returns the record
+    and host copies of the eager step's results, which the CPU-oracle leg
+    checks."""
+    S = Setup(replicas, "b1_1m", keep_kv=True)
+    torch, wl = S.torch, S.wl
+    for r in range(replicas):
+        S.step(r)
+    torch.cuda.synchronize()
+    eager = [t.cpu().numpy() for t in (S.idx, S.cnt, S.out, S.lse)]
+    calls = {name: time_call(S, fn, replicas) for name, fn in (
+        ("append_index_topk", S.append_index_topk), ("sparse_decode", S.decode),
+        ("step", S.step))}
+    L = int(S.lens.max())
+    nb = algorithmic_bytes(1, L, wl.H, wl.D, wl.Di, wl.K)
+    fused = nb["index_topk"] + nb["append"]
+    step_bytes = sum(nb.values())
+    fused_gbs = fused / (calls["append_index_topk"] * 1e-6) / 1e9
+    res = {"workload": f"b1_1m: batch 1, ctx {L}, 64 heads, latent 512 FP4, indexer dim 128, "
+                       "Top-K 2048, SWA 128, 3-sigma boost of 1% of the keys",
+           "calls_us": calls,
+           "queries_per_s": 1.0 / (calls["step"] * 1e-6),
+           "step_bytes": step_bytes,
+           "step_gbs": step_bytes / (calls["step"] * 1e-6) / 1e9,
+           "step_hbm_frac": step_bytes / (calls["step"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "roofline": {"kernel": "csa2_append_index_topk", "bound": "hbm",
+                        "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": fused_gbs / HBM_PEAK_GBS, "bytes_per_launch": fused,
+                        "launch_us": calls["append_index_topk"]},
+           "sparse_decode_gbs": nb["sparse_decode"] / (calls["sparse_decode"] * 1e-6) / 1e9,
+           "parity": "skipped (checked in the CPU-oracle leg)"}
+    check = {"q_idx": S.q_idx_h[0], "keys": S.keys[0], "kv": S.kv[0], "q": S.q_h[0],
+             "ring": S.ring_host[0], "sigma": S.sigma, "L": L, "K": wl.K, "gpu": eager}
+    del S
+    torch.cuda.empty_cache()
+    return res, check
 
 
 def scaled_calls(S: Setup) -> dict:
@@ -651,6 +748,36 @@ def scaled_parity(S: Setup, check) -> str:
     return "ok (sequence 0 against the oracle: Top-K bit-exact)"
 
 
+def long_context_parity(check) -> str:
+    """The b1_1m eager step against the oracle: Top-K bit-exact, outputs and
+    LSE within 2e-3."""
+    from oracle import attention as OA
+    from oracle import formats as OF
+    from oracle import select as OS
+
+    L, K = check["L"], check["K"]
+    g_idx, g_cnt, g_out, g_lse = (t[0] for t in check["gpu"])
+    idx, c = OS.topk(OS.indexer_scores(check["q_idx"], check["keys"][:L - 128]), L, K)
+    assert int(g_cnt) == c and np.array_equal(g_idx, idx), "b1_1m Top-K differs from the oracle"
+    sel = idx[:c]
+    o, lse = OA.sparse_decode(check["q"], check["sigma"], *OF.quantize_rows(check["kv"][sel]),
+                              check["ring"], sel, L)
+    err = max(float(np.max(np.abs(g_out - o))), float(np.max(np.abs(g_lse - lse))))
+    assert err <= 2e-3, f"b1_1m attention error {err:.3e}"
+    return f"ok (the sequence against the oracle: Top-K bit-exact, max-abs error {err:.1e})"
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(S: Setup, seconds: float, gpu=None):
     """The oracle's decode step (append of the new token, indexer scores,
     Top-K, dequantisation of the selected rows, merged attention) on the same
@@ -705,7 +832,7 @@ def cpu_baseline(S: Setup, seconds: float, gpu=None):
             "gbs": done / timed * per_query / 1e9,
             "sample": f"{done} whole decode steps (sequences of {WORKLOAD} in turn), "
                       f"{timed:.1f} s of timed oracle work; numpy float64, BLAS threads {threads}",
-            "host_cpus": len(os.sched_getaffinity(0))}, parity
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}, parity
 
 
 # ------------------------------------------------------------------ counters
@@ -818,14 +945,17 @@ def main() -> int:
     S = Setup(args.replicas)
     wl = S.wl
     wall, ev_ms, calls, spread, eager = gpu_bench(args, S)
-    chain = scaled = ragged = scaled_check = None
+    chain = scaled = ragged = scaled_check = long_ctx = long_check = None
     if not args.no_extras:
         chain = chain_calls(S)
         chain["schedule"] = schedule_calls(S)
         scaled, scaled_check = scaled_calls(S)
         log("b128_rag: building the ragged paged cache")
         ragged = ragged_calls()
+        log("b1_1m: building the 1M-token cache")
+        long_ctx, long_check = long_context_calls()
     copy_rate = copy_gbs(torch)
+    read_rate = read_gbs(torch, S.csa2)
     B, L, H, D, Di, K = wl.B, int(S.lens.max()), wl.H, wl.D, wl.Di, wl.K
     nbytes = algorithmic_bytes(B, L, H, D, Di, K)
     step_bytes = sum(nbytes.values())
@@ -840,12 +970,12 @@ def main() -> int:
     traffic = measured_traffic("append_index_topk")
     res = {
         "metric": "decode attention queries/sec and achieved HBM GB/s (% of peak) at 64K ctx",
-        "value": B * args.steps / wall,
+        "value": B / step_s,
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step": step_s * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -858,11 +988,14 @@ def main() -> int:
                    "window": 128,
                    "step": "append_index_topk (the 1-token/seq quantize_append fused into the Full "
                            "layer's scoring launch, then the Top-K) + sparse_decode",
-                   "replicas": args.replicas, "timing": "HIP graph replays"},
+                   "replicas": args.replicas,
+                   "timing": "HIP graph replays between HIP events on the kernels' stream"},
         "hbm_gbs": gbs,
         "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
         "step_bytes": step_bytes,
         "step_us_events": step_s * 1e6,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "sparse_decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
         "calls_us": calls,
         "calls_gbs": {"index_topk": topk_gbs, "append_index_topk": fused_gbs,
                       "sparse_decode": dec_gbs},
@@ -871,14 +1004,17 @@ def main() -> int:
                                "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                                "frac": dec_tflops / MFMA_F16_PEAK_TFLOPS},
         "copy_reference_gbs": copy_rate,
+        "read_reference_gbs": read_rate,
         "chain": chain,
         "scaled_indexer": scaled,
         "ragged_b128": ragged,
+        "long_b1_1m": long_ctx,
         "roofline": {"kernel": "csa2_append_index_topk ("
                                + ", ".join(STEP_KERNELS["append_index_topk"]) + ")",
                      "bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "frac_of_copy_reference": fused_gbs / copy_rate,
+                     "frac_of_read_reference": fused_gbs / read_rate,
                      "launch_us": calls["append_index_topk"], "bytes_per_launch": fused_bytes},
         "parity": "skipped (checked in the CPU-oracle leg)",
     }
@@ -889,6 +1025,9 @@ def main() -> int:
         log(f"parity: {res['parity']}")
         if scaled is not None and not args.no_parity:
             scaled["parity"] = scaled_parity(S, scaled_check)
+        if long_ctx is not None and not args.no_parity:
+            log("checking the b1_1m step against the oracle")
+            long_ctx["parity"] = long_context_parity(long_check)
     print(json.dumps(res), flush=True)
     return 0
 

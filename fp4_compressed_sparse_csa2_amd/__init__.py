@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     sparse_decode,
     sparse_decode_noalloc,
     store_key_scales,
+    stream_read,
     topk_merge,
     validate_selection,
     validate_window,

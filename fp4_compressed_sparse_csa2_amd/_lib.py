@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "csa2_page_bytes": (_c_sz, [_c_i32, _c_i32]),
             "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "csa2_workspace_init": (ctypes.c_int, [_c_vp, _c_sz, _c_vp]),
+            "csa2_stream_read": (ctypes.c_int, [_c_vp, _c_sz, _c_vp, _c_vp]),
             "csa2_quantize_append": (ctypes.c_int, [P, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
             "csa2_index_topk_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32]),
             "csa2_index_topk": (ctypes.c_int, [P, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp,
@@ -207,6 +208,17 @@ class Workspace:
 def workspace_init(ws: torch.Tensor) -> None:
     _check(lib().csa2_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(),
                                      _stream(ws.device)), "csa2_workspace_init")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """One read of every byte of the contiguous device tensor buf (a multiple
+    of 16 bytes), XOR-folded into sink (int32 [1]): the read-only bandwidth
+    reference a benchmark times beside the method's calls."""
+    if not buf.is_contiguous():
+        raise Csa2Error("stream_read: buf must be contiguous")
+    _need(sink, "sink", torch.int32, buf.device, (1,))
+    _check(lib().csa2_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                  sink.data_ptr(), _stream(buf.device)), "csa2_stream_read")
 
 
 def quantize_append(cache: Cache, x: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,

@@ -113,6 +113,13 @@ const char* csa2_status_string(int status) {
   }
 }
 
+int csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return CSA2_OK;
+  if (src == nullptr || sink == nullptr) return CSA2_E_NULL;
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0) return CSA2_E_SHAPE;
+  return status_of(csa2::run_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int csa2_workspace_init(void* ws, size_t bytes, void* stream) {
   if (bytes > 0 && ws == nullptr) return CSA2_E_NULL;
   return status_of(csa2::run_fill_zero(ws, bytes, static_cast<hipStream_t>(stream)));

@@ -97,6 +97,9 @@ constexpr uint32_t kWinNotF16 = 1u, kWinNotFinite = 2u;
 hipError_t run_validate_window(const CacheArgs& c, const int32_t* ctx_len, const uint16_t* swa,
                                uint32_t* flags, hipStream_t st);
 
+// One read of `bytes` (a multiple of 16) at src, XOR-folded into *sink.
+hipError_t run_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+
 hipError_t run_lse_merge(int n_parts, int batch, int H, int D, const float* outs,
                          const float* lses, float* out, float* lse, hipStream_t st);
 

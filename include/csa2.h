@@ -474,6 +474,21 @@ int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const floa
                         size_t ws_bytes, void* stream);
 
 /*
+ * csa2_stream_read -- a measurement aid, not a step of the method: reads
+ * `bytes` of device memory at src once with 16-byte non-temporal loads and
+ * XORs every word into *sink (device uint32; its old value is kept, so the
+ * result is defined but of no use beyond keeping the loads).  Timing it
+ * beside the method's calls gives the rate a plain read-only kernel reaches
+ * on this memory, the reference against which the calls' achieved rates are
+ * read: the method exists to cut the bytes one decode reads from HBM
+ * (neodrop.ai V4.1-Flash page, section 架构拆解 introduction; zulogic,
+ * section 9), and long-context decode is to be measured on its own
+ * (zulogic, section 10).  bytes must be a multiple of 16 and src 16-byte
+ * aligned.  Errors: CSA2_E_NULL, CSA2_E_SHAPE.
+ */
+int csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Context sharding with scaled keys: the same two steps as
  * csa2_index_topk_range + csa2_topk_merge, ranked by the values v_p.  The
  * merge is exact for the same reason (the order is total).

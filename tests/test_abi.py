@@ -27,7 +27,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -141,6 +141,14 @@ def test_sharded_scaled_calls_validate_before_launch(L):
                                           1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, 1, 40, 1, 1, None, 1, 1 << 30, None) == -2
     assert L.csa2_topk_merge_values(8, 2, 16, 1, 1, None, 8, 1, 1, None, 1, 1 << 30, None) == -1
+
+
+def test_stream_read_validates_before_launch(L):
+    assert L.csa2_stream_read(None, 0, None, None) == 0                # nothing to read
+    assert L.csa2_stream_read(None, 16, 1, None) == -1
+    assert L.csa2_stream_read(16, 16, None, None) == -1
+    assert L.csa2_stream_read(16, 24, 1, None) == -2                   # not a multiple of 16
+    assert L.csa2_stream_read(8, 16, 1, None) == -2                    # misaligned
 
 
 def test_validate_window_validates_before_launch(L):
