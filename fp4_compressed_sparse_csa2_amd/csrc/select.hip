@@ -56,26 +56,34 @@ __device__ __forceinline__ int sel_entries(const SelectArgs& a, int b) {
   return hi > a.p_begin ? hi - a.p_begin : 0;
 }
 
-// Output id of entry i: its position (p_begin + i), or the pool's position.
-__device__ __forceinline__ int32_t sel_id(const SelectArgs& a, int b, uint32_t i) {
-  return a.pool != nullptr ? a.pool[(size_t)b * a.P + i] : a.p_begin + (int32_t)i;
-}
-
 // The j-th selected entry c = {key, entry} of sequence b: its id, and its
-// score (or value) when the caller asked for them.
-template <typename KT>
+// score (or value) when the caller asked for them.  POOL (a Reindex layer):
+// the entry index goes out, and map_pool turns the list into pool positions
+// once it is complete.  No output store depends on a load, so that the
+// stores of an emission never wait for one another.
+template <typename KT, bool POOL>
 __device__ __forceinline__ void put_sel(const SelectArgs& a, int b, int j, uint2 c) {
-  a.out_idx[(size_t)b * a.K + j] = sel_id(a, b, c.y);
+  a.out_idx[(size_t)b * a.K + j] = POOL ? (int32_t)c.y : a.p_begin + (int32_t)c.y;
   if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = KT::out_word(c.x);
 }
 
+// The first `written` outputs of sequence b (entry indices, put_sel<.., true>
+// by this block) replaced by their pool positions.  All threads call.
+template <int NT>
+__device__ __forceinline__ void map_pool(const SelectArgs& a, int b, int written) {
+  __syncthreads();                               // the block's output stores are visible
+  int32_t* out = a.out_idx + (size_t)b * a.K;
+  const int32_t* pool = a.pool + (size_t)b * a.P;
+  for (int j = threadIdx.x; j < written; j += NT) out[j] = pool[out[j]];
+}
+
 // K = 0 or every entry selected: the first min(K, n) entries in order, then -1.
-template <typename KT>
+template <typename KT, bool POOL>
 __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, int nt) {
   int32_t* out = a.out_idx + (size_t)b * a.K;
   const int32_t* row = a.scores + (size_t)b * a.stride;
   for (int i = threadIdx.x; i < a.K; i += nt) {
-    out[i] = i < n ? sel_id(a, b, (uint32_t)i) : -1;
+    out[i] = i >= n ? -1 : (POOL ? a.pool[(size_t)b * a.P + i] : a.p_begin + i);
     if (a.out_sel_scores != nullptr)
       a.out_sel_scores[(size_t)b * a.K + i] = i < n ? KT::stored_out(row[i]) : 0;
   }
@@ -88,7 +96,7 @@ __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, in
 // of a wave reads 1 KB of consecutive scores.  In entry order the kept
 // entries of a wave are ordered by (i, lane, k); a lane's place among them
 // comes from ballots of its per-load counts.
-template <typename KT>
+template <typename KT, bool POOL>
 __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
   __shared__ uint2 list[kSingleListCap];
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   const int n = sel_entries(a, b);
   const int K = a.K;
   if (K == 0 || n <= K) {
-    select_all<KT>(a, b, n, kSelNT);
+    select_all<KT, POOL>(a, b, n, kSelNT);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -224,9 +232,14 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
     need_ties = sh_t3 >= 0 ? need_ties - sh_above3 : 0;
   }
   int32_t* out = a.out_idx + (size_t)b * K;
-  const int written = emit_in_order<kSelNT>(
-      get, total, tau, need_ties, K, wave_tot,
-      [&](int j, uint2 c) { put_sel<KT>(a, b, j, c); });
+  auto put = [&](int j, uint2 c) { put_sel<KT, POOL>(a, b, j, c); };
+  // (a list held in LDS is read with no global load on the way)
+  const int written =
+      total <= kSingleListCap
+          ? emit_in_order<kSelNT>([&](int f) -> uint2 { return list[f]; }, total, tau, need_ties,
+                                  K, wave_tot, put)
+          : emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot, put);
+  if constexpr (POOL) map_pool<kSelNT>(a, b, written);
   for (int j = written + tid; j < K; j += kSelNT) {
     out[j] = -1;
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 // Float keys take a third digit from an LDS histogram of the candidates
 // whose top 22 bits are the threshold's, counted from registers (direct) or
 // from the concatenated list (general).
-template <int SPL, typename KT>
+template <int SPL, typename KT, bool POOL>
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   constexpr int spl = SPL;
   __shared__ int offs[kMaxSelChunks + 1];
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   const int n = sel_entries(a, b);
   const int K = a.K;
   if (K == 0 || n <= K) {
-    select_all<KT>(a, b, n, kSelNT);
+    select_all<KT, POOL>(a, b, n, kSelNT);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -448,10 +461,10 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     for (int k = 0; k < spl; ++k) {
       if ((gtm >> k) & 1u) {
         const int slot = g + (t < need_ties ? t : need_ties);
-        if (slot < K) put_sel<KT>(a, b, slot, e[k]);
+        if (slot < K) put_sel<KT, POOL>(a, b, slot, e[k]);
         ++g;
       } else if ((tiem >> k) & 1u) {
-        if (t < need_ties && g + t < K) put_sel<KT>(a, b, g + t, e[k]);
+        if (t < need_ties && g + t < K) put_sel<KT, POOL>(a, b, g + t, e[k]);
         ++t;
       }
     }
@@ -519,9 +532,13 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     third_digit([&](auto add) {
       for (int f = tid; f < total; f += kSelNT) add(get(f).x);
     });
-    written = emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot,
-                                    [&](int j, uint2 c) { put_sel<KT>(a, b, j, c); });
+    auto put = [&](int j, uint2 c) { put_sel<KT, POOL>(a, b, j, c); };
+    written = total <= kListCap
+                  ? emit_in_order<kSelNT>([&](int f) -> uint2 { return list[f]; }, total, tau,
+                                          need_ties, K, wave_tot, put)
+                  : emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot, put);
   }
+  if constexpr (POOL) map_pool<kSelNT>(a, b, written);
   for (int j = written + tid; j < K; j += kSelNT) {
     out[j] = -1;
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
@@ -530,10 +547,10 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ host
-template <typename KT>
+template <typename KT, bool POOL>
 static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStream_t st) {
   if (max_entries <= kSingleMax) {
-    hipLaunchKernelGGL(select_single_kernel<KT>, dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_single_kernel<KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st, a);
     return hipGetLastError();
   }
   const int chunks = (max_entries + kFiltChunk - 1) / kFiltChunk;
@@ -545,19 +562,24 @@ static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStrea
   const long long share = (long long)a.K * kFiltChunk * 5;       // x 4 * max_entries
   const long long unit = (long long)max_entries * 4 * 64;
   if (share <= unit * 4)
-    hipLaunchKernelGGL((select_final_kernel<4, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<4, KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   else if (share <= unit * 8)
-    hipLaunchKernelGGL((select_final_kernel<8, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<8, KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st, a);
   else if (share <= unit * 12)
-    hipLaunchKernelGGL((select_final_kernel<12, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<12, KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((select_final_kernel<16, KT>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_final_kernel<16, KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st,
+                       a);
   return hipGetLastError();
 }
 
 hipError_t run_select(const SelectArgs& a, int max_entries, hipStream_t st) {
-  return a.float_keys ? run_select_keys<FloatKeys>(a, max_entries, st)
-                      : run_select_keys<IntKeys>(a, max_entries, st);
+  if (a.pool != nullptr)
+    return a.float_keys ? run_select_keys<FloatKeys, true>(a, max_entries, st)
+                        : run_select_keys<IntKeys, true>(a, max_entries, st);
+  return a.float_keys ? run_select_keys<FloatKeys, false>(a, max_entries, st)
+                      : run_select_keys<IntKeys, false>(a, max_entries, st);
 }
 
 }  // namespace csa2

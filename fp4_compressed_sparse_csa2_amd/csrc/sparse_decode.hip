@@ -54,6 +54,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 // Transposed LDS read: within each 16-lane group, lane i receives element
@@ -617,6 +618,63 @@ constexpr int kBlock8 = 512;
 constexpr int kStages = 3;           // LDS ring stages of FP4 tiles
 constexpr int kMaxRunTiles = 32;     // FP4 tiles of one 64-head block at most (row-key table)
 
+// Reads of a ring row written out here because the compiler cannot tell
+// the ring stages apart: before a plain LDS read of the ring it waits for
+// every global-to-LDS copy still in flight, the prefetch of the next two
+// tiles included, which would leave the ring nothing to overlap.  The caller
+// has waited for this tile's copies (vmcnt) and passed the block barrier.
+// Each read waits for its own data (one LDS wait per call).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+// Two 8-byte code words at p and p + 8.
+__device__ __forceinline__ void ring_codes2(const uint8_t* p, uint2& c0, uint2& c1) {
+  uint64_t a, b;
+  asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %2 offset:8\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b)
+               : "v"(lds_addr(p))
+               : "memory");
+  c0 = make_uint2((uint32_t)a, (uint32_t)(a >> 32));
+  c1 = make_uint2((uint32_t)b, (uint32_t)(b >> 32));
+}
+// NB scale bytes (2, 4 or 8) at p, as two words (the second 0 below 8).
+template <int NB>
+__device__ __forceinline__ void ring_scales(const uint8_t* p, uint32_t& s0, uint32_t& s1) {
+  s1 = 0u;
+  if constexpr (NB == 8) {
+    uint64_t v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+    s0 = (uint32_t)v;
+    s1 = (uint32_t)(v >> 32);
+  } else if constexpr (NB == 4) {
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(s0) : "v"(lds_addr(p)) : "memory");
+  } else {
+    static_assert(NB == 2, "2, 4 or 8 scale bytes");
+    asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(s0) : "v"(lds_addr(p)) : "memory");
+  }
+}
+
+// N LDS words (at the byte addresses a[]), read with one LDS wait and
+// without the compiler's wait for the copies in flight (see ring_read).
+template <int N>
+__device__ __forceinline__ void lds_words(const uint32_t (&a)[N], int (&w)[N]) {
+  static_assert(N >= 1 && N <= 3, "one to three words");
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(w[0]) : "v"(a[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(w[0]), "=&v"(w[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
+  }
+}
+
 // Every LDS access of this wave has completed, then the block barrier.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_sync() {
@@ -794,15 +852,32 @@ __global__ __launch_bounds__(kBlock8, 1) void sparse_decode64_kernel(
   // copies of tile f's rows into ring stage (f - fa) % kStages: this wave
   // issues copies c = wave, wave + 8, ... (< NCOPY) of the tile
   const int n_mine = (RG::NCOPY - wave + 7) / 8;  // copies per tile of this wave
+  constexpr int NC = (RG::NCOPY + 7) / 8;   // copies per wave and tile at most
   auto copy_tile = [&](int f) {
     uint8_t* stage = ring + ((f - fa) % kStages) * RG::STAGE;
+    // this wave's first slot of the tile, hidden from the compiler so that
+    // the slot arithmetic below is redone per call rather than kept in
+    // registers across the tile loop (where they would be spilled, and a
+    // spill reload waits for every copy in flight)
+    int k0 = wave * 64 + lane;
+    asm volatile("" : "+v"(k0));
+    // the row keys of this wave's copies first, then the copies
+    uint32_t ra[NC];
+    int rks[NC];
 #pragma unroll
-    for (int c0 = 0; c0 < (RG::NCOPY + 7) / 8; ++c0) {
+    for (int c0 = 0; c0 < NC; ++c0) {
+      const int c = c0 * 8 + wave;
+      const int row = c < RG::NCOPY ? (k0 + 512 * c0) / RG::PSPR : 0;
+      ra[c0] = lds_addr(&rk_lds[(f - fa) * kTile + row]);
+    }
+    lds_words<NC>(ra, rks);
+#pragma unroll
+    for (int c0 = 0; c0 < NC; ++c0) {
       const int c = c0 * 8 + wave;
       if (c < RG::NCOPY) {
-        const int k = c * 64 + lane;                       // slot of the tile
+        const int k = k0 + 512 * c0;                       // slot of the tile (c * 64 + lane)
         const int row = k / RG::PSPR, part = k - row * RG::PSPR;
-        const int rk = rk_lds[(f - fa) * kTile + row];
+        const int rk = rks[c0];
         const bool live = rk >= 0 && part < RG::SPR;       // else page 0, row 0 (pad slots,
         const int in_page = (rk & 63) * R + part * RG::CB; // invalid rows: never read)
         const uint8_t* src = pages + (live ? (size_t)(rk >> 6) * page_bytes + in_page : 0);
@@ -960,26 +1035,30 @@ __global__ __launch_bounds__(kBlock8, 1) void sparse_decode64_kernel(
     wait_tile(min(2, fb - 1 - f));
     lds_sync();                             // tile f is in LDS everywhere; X and P are free
     const uint8_t* rowp = my_row + ((f - fa) % kStages) * RG::STAGE;
-    const bool ok = rk_lds[(f - fa) * kTile + tok] >= 0;
-    // this lane's NG scale bytes (at D/2 + ch0/16) and code bytes (at ch0/2)
-    uint32_t sw0, sw1 = 0u;
-    if constexpr (NG == 8) {
-      const uint2 sv = *reinterpret_cast<const uint2*>(rowp + D / 2 + ch0 / 16);
-      sw0 = sv.x;
-      sw1 = sv.y;
-    } else if constexpr (NG == 4) {
-      sw0 = *reinterpret_cast<const uint32_t*>(rowp + D / 2 + ch0 / 16);
-    } else {
-      sw0 = *reinterpret_cast<const uint16_t*>(rowp + D / 2 + ch0 / 16);
+    // row keys of this lane's token and of the tokens 16tq + 4lg + i its
+    // logits belong to (-1: no row)
+    int rk_mine;
+    intx4 rk_q;
+    {
+      const uint32_t base = lds_addr(&rk_lds[(f - fa) * kTile + tq * 16]);
+      asm volatile("ds_read_b32 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk_mine), "=&v"(rk_q)
+                   : "v"(base + 4 * lc), "v"(base + 16 * lg)
+                   : "memory");
     }
+    const bool ok = rk_mine >= 0;
+    // this lane's NG scale bytes (at D/2 + ch0/16) and code bytes (at ch0/2)
+    uint32_t sw0, sw1;
+    ring_scales<NG>(rowp + D / 2 + ch0 / 16, sw0, sw1);
     half2v sc[4];
     e4m3x4_to_f16(ok ? sw0 : 0u, sc[0], sc[1]);
     if constexpr (NG > 4) e4m3x4_to_f16(ok ? sw1 : 0u, sc[2], sc[3]);
     floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    const uint2* cp = reinterpret_cast<const uint2*>(rowp + ch0 / 2);
+    uint2 cv[2];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const uint2 v = cp[g];
+      if ((g & 1) == 0) ring_codes2(rowp + ch0 / 2 + 8 * g, cv[0], cv[1]);
+      const uint2 v = cv[g & 1];
       const half2v spair = sc[g / 2];
       const half2v s2 = (g & 1) ? __builtin_shufflevector(spair, spair, 1, 1)
                                 : __builtin_shufflevector(spair, spair, 0, 0);
@@ -994,7 +1073,8 @@ __global__ __launch_bounds__(kBlock8, 1) void sparse_decode64_kernel(
       s[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf[0][2 * g + 1], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf[1][2 * g + 1], s[1], 0, 0, 0);
     }
-    const uint32_t vbits = (uint32_t)(__ballot(ok) >> (4 * lg)) & 0xFu;
+    const uint32_t vbits = (rk_q.x >= 0 ? 1u : 0u) | (rk_q.y >= 0 ? 2u : 0u) |
+                           (rk_q.z >= 0 ? 4u : 0u) | (rk_q.w >= 0 ? 8u : 0u);
     finish_tile(s, vbits);
   }
 

@@ -2,8 +2,9 @@
 indices bit-exact (ties to the lower position), on small shapes and the edge
 cases of the selection (planted ties, all-equal scores, K = 0, K >= number of
 candidates, context shorter than the window, kept candidates past the
-one-block selection's on-chip list, the multi-block plan for long sequences,
-paged ragged batches).  Full-size workloads are in test_gpu_configs.py."""
+on-chip lists, long sequences, paged ragged batches, top scores clustered
+in a few 1024-position blocks).  Full-size workloads are in
+test_gpu_configs.py."""
 import numpy as np
 import pytest
 import torch
@@ -47,7 +48,7 @@ def test_tiny_all_K(K):
     _check(gc, gen.idx_query(wl), K)
 
 
-@pytest.mark.parametrize("L", [0, 1, 127, 128, 129, 130, 191, 200])
+@pytest.mark.parametrize("L", [0, 1, 127, 128, 129, 130, 191, 200, 1152, 1153])
 def test_short_contexts(L):
     wl = gen.WORKLOADS["tiny"].with_(L=L)
     log(f"topk short L={L}")
@@ -80,8 +81,8 @@ def test_ties_go_to_lower_positions(mode):
 @pytest.mark.parametrize("mode", ["planted", "zeros"])
 def test_ties_past_the_lds_candidate_list(mode):
     """~20K candidates per sequence: with all scores equal every candidate is
-    kept, more than the one-block selection holds on chip, so the rest go
-    through its global overflow area."""
+    kept, more than the selections hold on chip, so the rest go through
+    their global overflow areas."""
     wl = gen.WORKLOADS["tiny"].with_(B=2, L=20000)
     log(f"topk ties L=20000 mode={mode}")
     gc = GpuCache(wl, keys_fn=_tie_keys(mode))
@@ -106,6 +107,37 @@ def test_paged_ragged_batch_di128():
     log("topk paged ragged B=16")
     gc = GpuCache(wl)
     _check(gc, gen.idx_query(wl), 512)
+
+
+def _clustered_keys(q, block_starts):
+    """Keys of 60% of the positions in the given 1024-position blocks made
+    small perturbations of the sequence's best key for its query q[b]: those
+    blocks then hold far more than their share of the Top-K, with distinct
+    scores spread over several top digits."""
+    def fn(b, k):
+        n = max(0, k.shape[0] - 128)
+        best = int(np.argmax(k[:n].astype(np.int64) @ q[b].astype(np.int64)))
+        rng = np.random.default_rng(100 + b)
+        out = k.copy()
+        for s0 in block_starts:
+            rows = np.arange(s0, min(s0 + 1024, n))
+            rows = rows[rng.random(rows.size) < 0.6]
+            noise = rng.integers(-3, 4, size=(rows.size, k.shape[1]))
+            out[rows] = np.clip(k[best].astype(np.int64) + noise, -127, 127).astype(np.int8)
+        return out
+    return fn
+
+
+def test_clustered_top_scores():
+    """Top scores packed into two 1024-position blocks, with distinct scores
+    over several top digits: the threshold digit and its ties come from a
+    few places, the rest of the sequence far below them."""
+    wl = gen.WORKLOADS["tiny"].with_(B=4, L=40000)
+    log("topk clustered L=40000")
+    q = gen.idx_query(wl)
+    gc = GpuCache(wl, keys_fn=_clustered_keys(q, [5 * 1024, 17 * 1024]))
+    for K in (300, 1000, 2048):
+        _check(gc, q, K)
 
 
 def test_deterministic_and_workspace_reuse():
