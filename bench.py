@@ -103,6 +103,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE counter runs of --counter-run "
                          "into profiles/traffic.json and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="instead of a run: per-kernel median durations and gaps of each "
+                         "workload's step in a rocprofv3 --kernel-trace CSV of this script "
+                         "(markdown tables)")
     ap.add_argument("--dcp", type=int, default=0, metavar="N",
                     help="instead of the headline bench: the 1M-token sequence cut over N "
                          "emulated devices (range Top-K per shard, merge, shard decodes, LSE "
@@ -843,7 +847,9 @@ STEP_KERNELS = {"append_index_topk": ("append_score_kernel", "select_single_kern
 
 
 def counter_run(args) -> int:
-    """Device copies of a known size, then eager steps, for the counter passes."""
+    """Device copies of a known size, then eager steps, for the counter passes
+    (the b8_64k step, or with --ragged-only the b128_rag step as its three
+    calls)."""
     import torch
     a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
     bb = torch.empty_like(a)
@@ -852,9 +858,14 @@ def counter_run(args) -> int:
         bb.copy_(a)
     torch.cuda.synchronize()
     del a, bb
-    S = Setup(args.replicas)
-    for i in range(args.warmup + args.steps):
-        S.step(i % args.replicas)
+    if args.ragged_only:
+        S = Setup(1, "b128_rag")
+        for i in range(args.warmup + args.steps):
+            S.step_unfused(0)
+    else:
+        S = Setup(args.replicas)
+        for i in range(args.warmup + args.steps):
+            S.step(i % args.replicas)
     torch.cuda.synchronize()
     print(json.dumps({"counter_run": True, "steps": args.steps, "calib_bytes": CALIB_BYTES,
                       "calib_copies": 3}), flush=True)
@@ -911,9 +922,77 @@ def traffic_from(fetch_dir: str, write_dir: str, steps: int) -> dict:
     return res
 
 
+# Kernel sequences of one step per workload in a trace of the default run:
+# (title, kernel-name patterns in launch order, grid rows of the first kernel).
+TRACE_STEPS = [
+    ("b8_64k step: csa2_append_index_topk + csa2_sparse_decode",
+     [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
+      r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode_kernel<512, 16, true>",
+      r"sparse_combine_kernel<512, 16>"], 9),
+    ("b1_1m step: csa2_append_index_topk + csa2_sparse_decode",
+     [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
+      r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode\w*_kernel<512[^>]*>",
+      r"sparse_combine_kernel<512, \d+>"], 2),
+    ("b128_rag csa2_index_topk",
+     [r"index_score_kernel<128, false>", r"select_filter_kernel<IntKeys>",
+      r"select_final_kernel<\d+, IntKeys, false>"], 128),
+    ("b128_rag csa2_sparse_decode",
+     [r"sparse_decode64_kernel<512>", r"sparse_combine_kernel<512, 64>"], None),
+    ("b8_64k csa2_reindex 8192 -> 2048",
+     [r"reindex_score_kernel<128, false>", r"select_single_kernel<IntKeys, true>"], None),
+]
+
+
+def trace_summary(path: str) -> str:
+    """Markdown tables of TRACE_STEPS from a rocprofv3 kernel-trace CSV:
+    every run of the kernel sequence, per kernel the median duration and the
+    median gap after the previous kernel, and the median whole run."""
+    import csv
+    import statistics
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"].split("(")[0].replace("void ", "").replace("csa2::", "")
+             for r in rows]
+    out = []
+    for title, seq, grid_y in TRACE_STEPS:
+        dur = [[] for _ in seq]
+        gap = [[] for _ in seq]
+        whole = []
+        i = 0
+        while i + len(seq) <= len(rows):
+            if (all(re.fullmatch(seq[k], names[i + k]) for k in range(len(seq))) and
+                    (grid_y is None or int(rows[i]["Grid_Size_Y"]) == grid_y)):
+                g = rows[i:i + len(seq)]
+                for k in range(len(seq)):
+                    dur[k].append(int(g[k]["End_Timestamp"]) - int(g[k]["Start_Timestamp"]))
+                    if k:
+                        gap[k].append(int(g[k]["Start_Timestamp"]) - int(g[k - 1]["End_Timestamp"]))
+                whole.append(int(g[-1]["End_Timestamp"]) - int(g[0]["Start_Timestamp"]))
+                i += len(seq)
+            else:
+                i += 1
+        out.append(f"{title}: {len(whole)} runs\n\n| kernel | median µs | median gap before µs |\n"
+                   "|---|---|---|")
+        for k in range(len(seq)):
+            if dur[k]:
+                g = f"{statistics.median(gap[k]) / 1e3:.2f}" if gap[k] else "-"
+                out.append(f"| `{names_of(seq[k])}` | {statistics.median(dur[k]) / 1e3:.2f} | {g} |")
+        if whole:
+            out.append(f"| whole run | {statistics.median(whole) / 1e3:.2f} | |")
+        out.append("")
+    return "\n".join(out)
+
+
+def names_of(pattern: str) -> str:
+    return pattern.replace("\\d+", "N").replace("\\w*", "").replace("[^>]*", "...")
+
+
 # ------------------------------------------------------------------ main
 def main() -> int:
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
     if args.traffic_from:
         rec = traffic_from(*args.traffic_from, args.steps)
         rec["command"] = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "

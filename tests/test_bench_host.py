@@ -49,3 +49,37 @@ def test_code_digest_ignores_comments_and_layout():
     c = "int f(int x) { return 3 * x; }"
     assert bench._code_tokens(a) == bench._code_tokens(b) != bench._code_tokens(c)
     assert len(bench.source_digest()) == 16
+
+
+def test_trace_summary_finds_each_step(tmp_path):
+    """A hand-made kernel trace: two b8_64k steps back to back (the second
+    with a 1 µs gap before its decode), an unrelated kernel between them, and
+    a b128 decode; the summary reports the medians of each sequence."""
+    hdr = ("Kind,Agent_Id,Queue_Id,Stream_Id,Thread_Id,Dispatch_Id,Kernel_Id,Kernel_Name,"
+           "Correlation_Id,Start_Timestamp,End_Timestamp,Grid_Size_X,Grid_Size_Y,Grid_Size_Z")
+    rows, t = [], 0
+
+    def k(name, dur_ns, grid_y=1, gap_ns=0):
+        nonlocal t
+        t += gap_ns
+        rows.append(f'K,1,1,0,1,{len(rows)},1,"void csa2::{name}(int)",1,{t},{t + dur_ns},1,{grid_y},1')
+        t += dur_ns
+
+    for gap in (0, 1000):
+        k("append_score_kernel<512, 128>", 13000, grid_y=9)
+        k("select_filter_kernel<csa2::IntKeys>", 5000)
+        k("select_final_kernel<4, csa2::IntKeys, false>", 6000)
+        k("sparse_decode_kernel<512, 16, true>", 13000, gap_ns=gap)
+        k("sparse_combine_kernel<512, 16>", 5000)
+        k("fill_zero_kernel", 2000)
+    k("sparse_decode64_kernel<512>", 70000)
+    k("sparse_combine_kernel<512, 64>", 15000)
+    path = tmp_path / "trace.csv"
+    path.write_text(hdr + "\n" + "\n".join(rows) + "\n")
+    out = bench.trace_summary(str(path))
+    assert "b8_64k step: csa2_append_index_topk + csa2_sparse_decode: 2 runs" in out
+    assert "| `sparse_decode_kernel<512, 16, true>` | 13.00 | 0.50 |" in out
+    assert "| whole run | 42.50 | |" in out
+    assert "b128_rag csa2_sparse_decode: 1 runs" in out
+    assert "| whole run | 85.00 | |" in out
+    assert "b1_1m step: csa2_append_index_topk + csa2_sparse_decode: 0 runs" in out
