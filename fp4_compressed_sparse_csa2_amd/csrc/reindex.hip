@@ -21,6 +21,8 @@
 namespace csa2 {
 
 constexpr int kREntries = 256;          // pool entries per block
+constexpr int kRPtCache = 1024;         // page-table entries staged in LDS (65536 positions)
+constexpr int kRPtPer = kRPtCache / kBlock;
 
 template <int DI, bool SCALED>
 __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
@@ -33,6 +35,7 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
   constexpr int LPP = DI / 16;
   constexpr int PPL = 64 / LPP;
   __shared__ uint32_t hist[kBins];
+  __shared__ int32_t pt_lds[kRPtCache];
 
   const int b = blockIdx.y;
   int c = pool_count[b];
@@ -42,29 +45,61 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
   if (e0 >= c || (!do_hist && out_scores == nullptr)) return;
   const int32_t* prow = pool + (size_t)b * P;
   int32_t* sc_row = scores + (size_t)b * stride;
-
-  if (do_hist) {
-    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
-    __syncthreads();
-  }
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const int wbase = e0 + wave * 64;
+
+  // The pool entries, the query and (up to kRPtCache pages) the sequence's
+  // page table are loaded together; the page of an entry is then an LDS
+  // read, so a key row is the second dependent trip, not the third.
+  const bool pt_in_lds = max_pages <= kRPtCache;
+  int pe[LPP];
+#pragma unroll
+  for (int j = 0; j < LPP; ++j) {       // entry wbase + j*PPL + lane/LPP
+    const int e = wbase + j * PPL + lane / LPP;
+    pe[j] = e < c ? prow[e] : -1;
+  }
+  const int4 qc = *reinterpret_cast<const int4*>(q_idx + (size_t)b * DI + (lane % LPP) * 16);
+  if (pt_in_lds) {
+    int ptv[kRPtPer];
+#pragma unroll
+    for (int i = 0; i < kRPtPer; ++i) {
+      const int k = threadIdx.x + i * kBlock;
+      ptv[i] = k < max_pages ? pt[k] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kRPtPer; ++i) pt_lds[threadIdx.x + i * kBlock] = ptv[i];
+  }
+  if (do_hist)
+    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+  if (pt_in_lds || do_hist) __syncthreads();       // block-uniform
+
+  // pages of the LPP entries first, then their key rows: every key load of
+  // the lane is in flight at once
+  int pg[LPP];
+  if (pt_in_lds) {
+#pragma unroll
+    for (int j = 0; j < LPP; ++j) {
+      const bool in = pe[j] >= 0 && pe[j] < max_pages * kPage;
+      const int g = pt_lds[in ? pe[j] / kPage : 0];
+      pg[j] = in ? g : -1;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < LPP; ++j)
+      pg[j] = (pe[j] >= 0 && pe[j] < max_pages * kPage) ? pt[pe[j] / kPage] : -1;
+  }
   uint4 v[LPP];
   bool ok[LPP];
   int srow = -1;                        // scaled: key-scale slot of the entry this lane keeps
 #pragma unroll
-  for (int j = 0; j < LPP; ++j) {       // entry wbase + j*PPL + lane/LPP
-    const int e = wbase + j * PPL + lane / LPP;
-    const int p = e < c ? prow[e] : -1;
-    const int pg = (p >= 0 && p < max_pages * kPage) ? pt[p / kPage] : -1;
-    ok[j] = pg >= 0 && pg < num_pages;
+  for (int j = 0; j < LPP; ++j) {
+    const int p = pe[j];
+    ok[j] = pg[j] >= 0 && pg[j] < num_pages;
     if (ok[j])
-      v[j] = *reinterpret_cast<const uint4*>(pages + (size_t)pg * page_bytes + keys_off +
+      v[j] = *reinterpret_cast<const uint4*>(pages + (size_t)pg[j] * page_bytes + keys_off +
                                              (p % kPage) * DI + (lane % LPP) * 16);
-    if (SCALED && (lane % LPP) == j && ok[j]) srow = pg * kPage + p % kPage;
+    if (SCALED && (lane % LPP) == j && ok[j]) srow = pg[j] * kPage + p % kPage;
   }
   float ks = 0.0f;
   if constexpr (SCALED) ks = srow >= 0 ? key_scales[srow] : 0.0f;
@@ -104,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void reindex_score_kernel(
   }
   if (do_hist) {
     __syncthreads();
-    uint32_t* g = ctrl + (size_t)b * kCtrlWords;
+    // block i adds into histogram replica i % kHistReps
+    uint32_t* g = ctrl + (size_t)b * kCtrlWords + (size_t)(blockIdx.x % kHistReps) * kBins;
     for (int i = threadIdx.x; i < kBins; i += kBlock) {
       const uint32_t h = hist[i];
       if (h) atomicAdd(&g[i], h);

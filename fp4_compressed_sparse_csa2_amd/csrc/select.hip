@@ -59,12 +59,18 @@ __device__ __forceinline__ int sel_entries(const SelectArgs& a, int b) {
 // The j-th selected entry c = {key, entry} of sequence b: its id, and its
 // score (or value) when the caller asked for them.  POOL (a Reindex layer):
 // the entry index goes out, and map_pool turns the list into pool positions
-// once it is complete.  No output store depends on a load, so that the
+// once it is complete (the one-block kernel holds the pool row in LDS and
+// writes positions directly).  No output store depends on a load, so that the
 // stores of an emission never wait for one another.
+template <typename KT>
+__device__ __forceinline__ void put_id(const SelectArgs& a, int b, int j, int32_t id,
+                                       uint32_t key) {
+  a.out_idx[(size_t)b * a.K + j] = id;
+  if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = KT::out_word(key);
+}
 template <typename KT, bool POOL>
 __device__ __forceinline__ void put_sel(const SelectArgs& a, int b, int j, uint2 c) {
-  a.out_idx[(size_t)b * a.K + j] = POOL ? (int32_t)c.y : a.p_begin + (int32_t)c.y;
-  if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * a.K + j] = KT::out_word(c.x);
+  put_id<KT>(a, b, j, POOL ? (int32_t)c.y : a.p_begin + (int32_t)c.y, c.x);
 }
 
 // The first `written` outputs of sequence b (entry indices, put_sel<.., true>
@@ -100,6 +106,7 @@ template <typename KT, bool POOL>
 __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
   __shared__ uint2 list[kSingleListCap];
+  __shared__ int32_t pool_lds[POOL ? kSingleMax : 1];   // the sequence's pool row
   __shared__ int scan_scratch[kSelWaves];
   __shared__ int round_tot[2][kSelWaves];
   __shared__ int2 wave_tot[kSelWaves];
@@ -129,10 +136,30 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
       v[i] = *reinterpret_cast<const uint4*>(row + (e0 < n ? e0 : 0));
     }
   };
+  // POOL: the pool row goes to LDS, its loads in flight with the first
+  // round's and the histogram's, so that the emission writes pool positions
+  // with no global load on the way
+  constexpr int kPoolPer = POOL ? kSingleMax / kSelNT : 1;
+  int32_t pv[kPoolPer];
+  if constexpr (POOL) {
+    const int32_t* prow = a.pool + (size_t)b * a.P;
+#pragma unroll
+    for (int i = 0; i < kPoolPer; ++i) {
+      const int e = tid + i * kSelNT;
+      pv[i] = e < n ? prow[e] : -1;
+    }
+  }
   uint4 va[kSelLd], vb[kSelLd];
   load_round(va, 0);
   const DigitBins<kSelNT> bins = load_digit_bins<kSelNT, kHistReps>(h1);
   for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
+  if constexpr (POOL) {
+#pragma unroll
+    for (int i = 0; i < kPoolPer; ++i) {
+      const int e = tid + i * kSelNT;
+      if (e < n) pool_lds[e] = pv[i];
+    }
+  }
   find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
   // digit >= t1  <=>  score >= lo (score_key folds only the top score, which
@@ -232,14 +259,15 @@ __global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
     need_ties = sh_t3 >= 0 ? need_ties - sh_above3 : 0;
   }
   int32_t* out = a.out_idx + (size_t)b * K;
-  auto put = [&](int j, uint2 c) { put_sel<KT, POOL>(a, b, j, c); };
+  auto put = [&](int j, uint2 c) {
+    put_id<KT>(a, b, j, POOL ? pool_lds[c.y] : a.p_begin + (int32_t)c.y, c.x);
+  };
   // (a list held in LDS is read with no global load on the way)
   const int written =
       total <= kSingleListCap
           ? emit_in_order<kSelNT>([&](int f) -> uint2 { return list[f]; }, total, tau, need_ties,
                                   K, wave_tot, put)
           : emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot, put);
-  if constexpr (POOL) map_pool<kSelNT>(a, b, written);
   for (int j = written + tid; j < K; j += kSelNT) {
     out[j] = -1;
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
