@@ -73,30 +73,51 @@ __device__ __forceinline__ int sum_oct(int v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP moves (no LDS
+// round trip): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row; then
+// lane 15 of rows 0 and 2 is added to rows 1 and 3 (row_bcast:15), and lane
+// 31, the total of rows 0-1, to rows 2 and 3 (row_bcast:31).  A lane whose
+// source lies outside its row, or whose row is masked off, adds 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+// Given the NT/64 wave totals in `scratch` (after a barrier): the sum of the
+// totals of the waves before the calling one, and of all of them, both
+// wave-uniform.  Lane w < NT/64 reads total w; one wave scan and two lane
+// reads replace a per-wave loop over the totals.
+template <int NT>
+__device__ __forceinline__ int2 waves_before_and_total(const int* scratch) {
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 64, "one total per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int x = wave_inclusive_scan(lane < NW ? scratch[lane] : 0);
+  const int before = wave == 0 ? 0 : __builtin_amdgcn_readlane(x, wave - 1);
+  return make_int2(before, __builtin_amdgcn_readlane(x, NW - 1));
+}
+
 // Exclusive prefix sum over an NT-thread block; returns the prefix, sets *total.
 // `scratch` must hold NT/64 ints of shared memory.  Contains barriers: every
-// thread of the block must call it.
-template <int NT = kBlock>
+// thread of the block must call it.  SYNC_AFTER = false leaves out the
+// closing barrier: the caller then passes a barrier before `scratch` is
+// written again.
+template <int NT = kBlock, bool SYNC_AFTER = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    int s = scratch[w];
-    base += (w < wave) ? s : 0;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
+  const int2 bt = waves_before_and_total<NT>(scratch);
+  if constexpr (SYNC_AFTER) __syncthreads();
+  *total = bt.y;
+  return bt.x + x - v;
 }
 
 // ------------------------------------------------------------------ FP8 / FP4

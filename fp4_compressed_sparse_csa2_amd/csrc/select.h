@@ -79,7 +79,8 @@ __device__ inline void find_digit_in(const DigitBins<NT>& d, int need, int* scan
     *above_out = 0;
   }
   int total;
-  const int excl = block_exclusive_scan<NT>(s, scan_scratch, &total);
+  // (scan_scratch is next written after the closing barrier below)
+  const int excl = block_exclusive_scan<NT, false>(s, scan_scratch, &total);
   if (excl < need && need <= excl + s) {
     int run = excl;
 #pragma unroll

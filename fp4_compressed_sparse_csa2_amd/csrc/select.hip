@@ -12,14 +12,12 @@
 // bits of the biased 22-bit key (built by the scoring kernel).  Two plans, no
 // cross-block synchronisation inside a kernel (visibility comes from kernel
 // boundaries):
-//   single  - up to kSingleMax entries: one block per sequence finds the
-//             K-th largest top digit t1 and reads the scores once, in rounds
-//             of 16K entries where each wave streams a contiguous run with
-//             1 KB loads (the next round's loads in flight while one is
-//             compacted), keeping the entries with digit >= t1 in entry
-//             order (ballot prefix counts in the wave, one barrier per
-//             round); then it histograms the low digit of the kept entries
-//             equal to t1, fixes the exact threshold and emits in order.
+//   single  - up to kSingleMax entries: one block per sequence holds them
+//             all in registers (one 16-byte load row of 16 KB per step),
+//             finds the K-th largest top digit t1, histograms the low digit
+//             of the entries whose top digit is t1, fixes the exact
+//             threshold and gives each selected entry its output slot from
+//             one block scan of per-thread counts.
 //   filter  - longer sequences: 4096-entry blocks keep their digit >= t1
 //   + final   entries, in order, in their own slots; then one block per
 //             sequence concatenates the slot lists (already in order),
@@ -33,11 +31,7 @@ namespace csa2 {
 
 constexpr int kSelNT = 1024;                     // threads of the one-block-per-sequence kernels
 constexpr int kSelWaves = kSelNT / 64;
-constexpr int kSelLd = 4;                        // 16-byte loads per lane per round
-constexpr int kWaveRun = 64 * 4 * kSelLd;        // 1024 entries per wave per round
-constexpr int kSelRound = kSelWaves * kWaveRun;  // 16384 entries (64 KB) per round
 constexpr int kListCap = 6144;                   // candidates the final kernel keeps in LDS
-constexpr int kSingleListCap = 6144;             // candidates the single kernel keeps in LDS
 constexpr int kFiltPer = 16;                     // entries per thread in the filter kernel
 constexpr int kFiltChunk = kBlock * kFiltPer;    // 4096 entries per filter block
 
@@ -97,184 +91,234 @@ __device__ __forceinline__ void select_all(const SelectArgs& a, int b, int n, in
 }
 
 // ------------------------------------------------------------------ single
-// Round r, wave w streams entries [r*16384 + 1024w, +1024): lane l's load i
-// holds the four entries at 256i + 4l of that run, so every load instruction
-// of a wave reads 1 KB of consecutive scores.  In entry order the kept
-// entries of a wave are ordered by (i, lane, k); a lane's place among them
-// comes from ballots of its per-load counts.
+// Up to kSingleMax entries, all held in registers by a block of kSingleNT
+// threads.  Thread t holds entries 4096j + 4t + k (j < 4, k < 4): row j of
+// the block's loads reads 16 KB of consecutive scores, 1 KB per wave
+// instruction (rows past the last entry are not loaded).  With the top digit t1 from
+// the scoring kernel's histogram, the entries whose top digit is t1
+// histogram their second digit in LDS (float keys: then those on the
+// threshold's top 22 bits their third), which fixes the threshold key tau and
+// how many entries equal to it are taken.  One block scan of each thread's
+// per-row (above, tie) counts then gives every selected entry its output slot
+// in entry order: no candidate list is built.  POOL: the pool row is staged in
+// LDS (its loads in flight with the scores') and the slots get pool positions.
+constexpr int kSingleNT = 1024;                      // threads of the one-block kernel
+constexpr int kSingleWaves = kSingleNT / 64;
+constexpr int kRegRow = 4 * kSingleNT;                // entries per load row
+constexpr int kRegRows = kSingleMax / kRegRow;        // 4 rows of 4096 entries
+static_assert(kRegRow <= 0xFFFF, "a row prefix fits a packed half");
+
 template <typename KT, bool POOL>
-__global__ __launch_bounds__(kSelNT) void select_single_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSingleNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
-  __shared__ uint2 list[kSingleListCap];
   __shared__ int32_t pool_lds[POOL ? kSingleMax : 1];   // the sequence's pool row
-  __shared__ int scan_scratch[kSelWaves];
-  __shared__ int round_tot[2][kSelWaves];
-  __shared__ int2 wave_tot[kSelWaves];
+  __shared__ int scan_scratch[kSingleWaves];
+  __shared__ int row_scan[kRegRows][kSingleWaves];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2, sh_t3, sh_above3;
 
   const int b = blockIdx.x;
   const int n = sel_entries(a, b);
   const int K = a.K;
   if (K == 0 || n <= K) {
-    select_all<KT, POOL>(a, b, n, kSelNT);
+    select_all<KT, POOL>(a, b, n, kSingleNT);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* h1 = a.hist1 + (size_t)b * kCtrlWords;
   const int32_t* row = a.scores + (size_t)b * a.stride;
-  uint2* ovf = a.cand + (size_t)b * a.stride;
-  const int rounds = (n + kSelRound - 1) / kSelRound;
+  const int nrows = (n + kRegRow - 1) / kRegRow;        // load rows holding entries
 
+  // POOL: with P a multiple of 4 and a 16-byte aligned pool, the row is read
+  // in rows of 16-byte loads like the scores (entries 4096j + 4t .. +3; a
+  // load that starts below n <= P then ends inside the row), else entry by
+  // entry
+  constexpr int kPoolPer = POOL ? kSingleMax / kSingleNT : 1;
+  int32_t pv[kPoolPer];
+  const int32_t* prow = POOL ? a.pool + (size_t)b * a.P : nullptr;
+  const bool pool16 =
+      POOL && (a.P & 3) == 0 && (reinterpret_cast<uintptr_t>(a.pool) & 15u) == 0u;
+  if constexpr (POOL) {
+    if (pool16) {
+#pragma unroll
+      for (int j = 0; j < kRegRows; ++j) {
+        if (j >= nrows) break;
+        const int e0 = j * kRegRow + 4 * tid;
+        const int4 q = *reinterpret_cast<const int4*>(prow + (e0 < n ? e0 : 0));
+        pv[4 * j] = q.x;
+        pv[4 * j + 1] = q.y;
+        pv[4 * j + 2] = q.z;
+        pv[4 * j + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPoolPer; ++i) {
+        const int e = tid + i * kSingleNT;
+        pv[i] = prow[e < n ? e : 0];
+      }
+    }
+  }
   // Entry indices of a load are multiples of 4 and the row stride a multiple
   // of 64, so a load that starts below n lies inside the row; loads that
   // start at or past n read entry 0 instead and are masked.
-  auto load_round = [&](uint4 (&v)[kSelLd], int r) {
-    const int base = r * kSelRound + wave * kWaveRun + 4 * lane;
+  uint4 v[kRegRows];
 #pragma unroll
-    for (int i = 0; i < kSelLd; ++i) {
-      const int e0 = base + 256 * i;
-      v[i] = *reinterpret_cast<const uint4*>(row + (e0 < n ? e0 : 0));
-    }
-  };
-  // POOL: the pool row goes to LDS, its loads in flight with the first
-  // round's and the histogram's, so that the emission writes pool positions
-  // with no global load on the way
-  constexpr int kPoolPer = POOL ? kSingleMax / kSelNT : 1;
-  int32_t pv[kPoolPer];
-  if constexpr (POOL) {
-    const int32_t* prow = a.pool + (size_t)b * a.P;
-#pragma unroll
-    for (int i = 0; i < kPoolPer; ++i) {
-      const int e = tid + i * kSelNT;
-      pv[i] = e < n ? prow[e] : -1;
-    }
+  for (int j = 0; j < kRegRows; ++j) {
+    if (j >= nrows) break;
+    const int e0 = j * kRegRow + 4 * tid;
+    v[j] = *reinterpret_cast<const uint4*>(row + (e0 < n ? e0 : 0));
   }
-  uint4 va[kSelLd], vb[kSelLd];
-  load_round(va, 0);
-  const DigitBins<kSelNT> bins = load_digit_bins<kSelNT, kHistReps>(h1);
-  for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
+  const DigitBins<kSingleNT> bins = load_digit_bins<kSingleNT, kHistReps>(h1);
+  for (int i = tid; i < kBins; i += kSingleNT) hist2[i] = 0u;
   if constexpr (POOL) {
+    if (pool16) {
 #pragma unroll
-    for (int i = 0; i < kPoolPer; ++i) {
-      const int e = tid + i * kSelNT;
-      if (e < n) pool_lds[e] = pv[i];
-    }
-  }
-  find_digit_in<kSelNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
-  const uint32_t t1 = (uint32_t)sh_t1;
-  // digit >= t1  <=>  score >= lo (score_key folds only the top score, which
-  // is above every threshold a digit can set); for float keys, key >= lo_key
-  const int lo = sh_t1 < 0 ? INT_MAX : (int)(t1 << 11) - kKeyBias;
-  const bool have_t1 = sh_t1 >= 0;
-  const uint32_t lo_key = t1 << KT::kTopShift;
-  auto kept = [&](int w) -> bool {
-    if constexpr (KT::kThree) return have_t1 && (uint32_t)w >= lo_key;
-    else return w >= lo;
-  };
-
-  int total = 0;
-  // kept-entry mask of load i (bit k: entry e0 + k) and its in-wave counts
-  auto keep_mask = [&](const uint4& v, int e0) -> uint32_t {
-    const int w[4] = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-    uint32_t m = 0;
+      for (int j = 0; j < kRegRows; ++j) {
+        if (j >= nrows) break;
+        const int e0 = j * kRegRow + 4 * tid;
+        if (e0 < n)
+          *reinterpret_cast<int4*>(pool_lds + e0) =
+              make_int4(pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]);
+      }
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) m |= (kept(w[k]) && e0 + k < n) ? (1u << k) : 0u;
-    return m;
-  };
-  auto keep_round = [&](const uint4 (&v)[kSelLd], int r) {
-    const int base = r * kSelRound + wave * kWaveRun + 4 * lane;
-    // pass 1: the wave's number of kept entries
-    int wtot = 0;
-#pragma unroll
-    for (int i = 0; i < kSelLd; ++i) {
-      const uint32_t c = __builtin_popcount(keep_mask(v[i], base + 256 * i));
-      wtot += (int)(__popcll(__ballot(c & 1u)) + 2 * __popcll(__ballot(c & 2u)) +
-                    4 * __popcll(__ballot(c & 4u)));
-    }
-    if (lane == 0) round_tot[r & 1][wave] = wtot;
-    __syncthreads();
-    int woff = total, rtot = 0;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int t = round_tot[r & 1][w];
-      woff += w < wave ? t : 0;
-      rtot += t;
-    }
-    // pass 2: place them in entry order (load i, then lane, then k)
-    if (wtot > 0) {                                     // wave-uniform
-#pragma unroll
-      for (int i = 0; i < kSelLd; ++i) {
-        const int e0 = base + 256 * i;
-        const uint32_t m = keep_mask(v[i], e0);
-        const uint32_t c = __builtin_popcount(m);
-        const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-        int slot = woff + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
-        woff += (int)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
-        const int w[4] = {(int)v[i].x, (int)v[i].y, (int)v[i].z, (int)v[i].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if ((m >> k) & 1u) {
-            const uint2 cc = make_uint2(KT::key(w[k]), (uint32_t)(e0 + k));
-            if (slot < kSingleListCap) list[slot] = cc; else ovf[slot] = cc;
-            ++slot;
-          }
-        }
+      for (int i = 0; i < kPoolPer; ++i) {
+        const int e = tid + i * kSingleNT;
+        if (e < n) pool_lds[e] = pv[i];
       }
     }
-    total += rtot;
-  };
-  // two round buffers: round r + 1 is in flight while round r is compacted
-  for (int r = 0; r < rounds; r += 2) {
-    if (r + 1 < rounds) load_round(vb, r + 1);
-    keep_round(va, r);
-    if (r + 1 >= rounds) break;
-    if (r + 2 < rounds) load_round(va, r + 2);
-    keep_round(vb, r + 1);
   }
-  __syncthreads();
-  auto get = [&](int f) -> uint2 { return f < kSingleListCap ? list[f] : ovf[f]; };
-  // second-digit histogram of the kept entries whose top digit is t1
-  for (int f = tid; f < total; f += kSelNT) {
-    const uint2 c = get(f);
-    if ((c.x >> KT::kTopShift) == t1) atomicAdd(&hist2[KT::mid(c.x)], 1u);
-  }
-  __syncthreads();
+  find_digit_in<kSingleNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
+  const bool have_t1 = sh_t1 >= 0;
+  const uint32_t t1 = (uint32_t)sh_t1;
 
-  find_digit<kSelNT>(hist2, K - sh_above1, scan_scratch, &sh_t2, &sh_above2);
-  uint32_t tau = (t1 << 11) | (uint32_t)sh_t2;
+  // keys of the held entries (rows past n are skipped, block-uniformly) and
+  // 4-bit masks of the live ones, and of those whose top digit is t1
+  uint32_t key[kRegRows][4];
+  uint32_t live[kRegRows];
+#pragma unroll
+  for (int j = 0; j < kRegRows; ++j) {
+    live[j] = 0u;
+    if (j >= nrows) continue;
+    const int w[4] = {(int)v[j].x, (int)v[j].y, (int)v[j].z, (int)v[j].w};
+    const int lim = n - j * kRegRow - 4 * tid;          // live entries of the four
+    live[j] = lim >= 4 ? 0xFu : (lim > 0 ? (1u << lim) - 1u : 0u);
+    uint32_t at_t1 = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      key[j][k] = KT::key(w[k]);
+      at_t1 |= (key[j][k] >> KT::kTopShift) == t1 ? 1u << k : 0u;
+    }
+    at_t1 = have_t1 ? at_t1 & live[j] : 0u;
+    if (at_t1 != 0u) {                                  // second digit, few entries
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((at_t1 >> k) & 1u) atomicAdd(&hist2[KT::mid(key[j][k])], 1u);
+    }
+  }
+  __syncthreads();
+  find_digit<kSingleNT>(hist2, K - sh_above1, scan_scratch, &sh_t2, &sh_above2);
+  uint32_t tau = have_t1 ? (t1 << 11) | (uint32_t)sh_t2 : 0xFFFFFFFFu;
   int need_ties = K - sh_above1 - sh_above2;
   if constexpr (KT::kThree) {
     // third digit: histogram (in hist2, whose bins every thread has read) of
-    // the kept entries whose top 22 bits are the threshold's
-    for (int i = tid; i < kBins; i += kSelNT) hist2[i] = 0u;
+    // the entries whose top 22 bits are the threshold's
+    for (int i = tid; i < kBins; i += kSingleNT) hist2[i] = 0u;
     __syncthreads();
-    const uint32_t pre = sh_t2 >= 0 ? tau : 0xFFFFFFFFu;
-    for (int f = tid; f < total; f += kSelNT) {
-      const uint2 c = get(f);
-      if ((c.x >> KT::kLowBits) == pre) atomicAdd(&hist2[KT::low(c.x)], 1u);
+    const uint32_t pre = have_t1 && sh_t2 >= 0 ? tau : 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < kRegRows; ++j) {
+      if (j >= nrows) continue;
+      uint32_t at = 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) at |= (key[j][k] >> KT::kLowBits) == pre ? 1u << k : 0u;
+      at &= live[j];
+      if (at != 0u) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if ((at >> k) & 1u) atomicAdd(&hist2[KT::low(key[j][k])], 1u);
+      }
     }
     __syncthreads();
-    find_digit<kSelNT>(hist2, need_ties, scan_scratch, &sh_t3, &sh_above3);
+    find_digit<kSingleNT>(hist2, need_ties, scan_scratch, &sh_t3, &sh_above3);
     tau = sh_t3 >= 0 ? (pre << KT::kLowBits) | (uint32_t)sh_t3 : 0xFFFFFFFFu;
     need_ties = sh_t3 >= 0 ? need_ties - sh_above3 : 0;
   }
+
+  // per row: masks of this thread's entries above tau and equal to it, and
+  // their counts packed as above + (ties << 16) (a row prefix is at most
+  // kRegRow, so the halves never carry)
+  uint32_t gt[kRegRows], tie[kRegRows];
+  int cnt[kRegRows], inc[kRegRows];
+#pragma unroll
+  for (int j = 0; j < kRegRows; ++j) {
+    gt[j] = tie[j] = 0u;
+    cnt[j] = inc[j] = 0;
+    if (j >= nrows) continue;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      gt[j] |= key[j][k] > tau ? 1u << k : 0u;
+      tie[j] |= key[j][k] == tau ? 1u << k : 0u;
+    }
+    gt[j] &= live[j];
+    tie[j] &= live[j];
+    cnt[j] = __builtin_popcount(gt[j]) + (__builtin_popcount(tie[j]) << 16);
+    inc[j] = wave_inclusive_scan(cnt[j]);
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < kRegRows; ++j) row_scan[j][wave] = inc[j];
+  }
+  __syncthreads();
+  int before[kRegRows], tot[kRegRows];
+#pragma unroll
+  for (int j = 0; j < kRegRows; ++j) {
+    before[j] = tot[j] = 0;
+    if (j >= nrows) continue;
+    const int2 bt = waves_before_and_total<kSingleNT>(row_scan[j]);
+    before[j] = bt.x;
+    tot[j] = bt.y;
+  }
+  // emit: the selected entries of a thread's row take consecutive slots,
+  // starting after every selection before them in entry order; ties are
+  // taken in entry order until need_ties of them are
+  int g0 = 0, t0 = 0;                                 // over the rows before j
+#pragma unroll
+  for (int j = 0; j < kRegRows; ++j) {
+    if (j >= nrows) continue;
+    const int pre = before[j] + inc[j] - cnt[j];      // this thread's row prefix
+    const int gb = g0 + (pre & 0xFFFF), tb = t0 + (pre >> 16);
+    uint32_t sel = gt[j];
+    int r = tb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool t = (tie[j] >> k) & 1u;
+      sel |= (t && r < need_ties) ? 1u << k : 0u;
+      r += t ? 1 : 0;
+    }
+    const int slot0 = gb + (tb < need_ties ? tb : need_ties);
+    if (sel != 0u) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int slot = slot0 + __builtin_popcount(sel & ((1u << k) - 1u));
+        if (((sel >> k) & 1u) && slot < K) {
+          const int e = j * kRegRow + 4 * tid + k;
+          put_id<KT>(a, b, slot, POOL ? pool_lds[e] : a.p_begin + e, key[j][k]);
+        }
+      }
+    }
+    g0 += tot[j] & 0xFFFF;
+    t0 += tot[j] >> 16;
+  }
+  const int taken = g0 + (t0 < need_ties ? t0 : need_ties);
+  const int written = taken < K ? taken : K;
   int32_t* out = a.out_idx + (size_t)b * K;
-  auto put = [&](int j, uint2 c) {
-    put_id<KT>(a, b, j, POOL ? pool_lds[c.y] : a.p_begin + (int32_t)c.y, c.x);
-  };
-  // (a list held in LDS is read with no global load on the way)
-  const int written =
-      total <= kSingleListCap
-          ? emit_in_order<kSelNT>([&](int f) -> uint2 { return list[f]; }, total, tau, need_ties,
-                                  K, wave_tot, put)
-          : emit_in_order<kSelNT>(get, total, tau, need_ties, K, wave_tot, put);
-  for (int j = written + tid; j < K; j += kSelNT) {
+  for (int j = written + tid; j < K; j += kSingleNT) {
     out[j] = -1;
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
   }
   if (tid == 0) a.out_count[b] = written;
   uint4* h4 = reinterpret_cast<uint4*>(h1);     // the histogram replicas, for the next call
-  for (int i = tid; i < kCtrlHist2 / 4; i += kSelNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < kCtrlHist2 / 4; i += kSingleNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------------ filter
@@ -578,7 +622,8 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
 template <typename KT, bool POOL>
 static hipError_t run_select_keys(const SelectArgs& a, int max_entries, hipStream_t st) {
   if (max_entries <= kSingleMax) {
-    hipLaunchKernelGGL((select_single_kernel<KT, POOL>), dim3(a.batch), dim3(kSelNT), 0, st, a);
+    hipLaunchKernelGGL((select_single_kernel<KT, POOL>), dim3(a.batch), dim3(kSingleNT), 0, st,
+                       a);
     return hipGetLastError();
   }
   const int chunks = (max_entries + kFiltChunk - 1) / kFiltChunk;

@@ -1,6 +1,7 @@
 """GPU parity of csa2_reindex: the Reindex layer's scores and Top-K' over the
 Full layer's pool, bit-exact against the oracle (pool smaller than K',
-K' = P, pools from short contexts padded with -1, planted ties)."""
+K' = P, pools from short contexts padded with -1, planted ties, pool lengths
+around the one-block selection's load rows and past its limit)."""
 import numpy as np
 import pytest
 import torch
@@ -40,6 +41,17 @@ def _chain(gc: GpuCache, K_full: int, K2: int):
 def test_chain_small(K_full, K2):
     wl = gen.WORKLOADS["tiny"].with_(B=3, L=6000, Di=128)
     log(f"reindex K_full={K_full} K2={K2}")
+    _chain(GpuCache(wl), K_full, K2)
+
+
+@pytest.mark.parametrize("K_full,K2", [(1023, 300), (4097, 1000), (4099, 4098), (12290, 3000),
+                                       (16383, 2048), (16384, 5000), (20000, 2048)])
+def test_chain_pool_sizes(K_full, K2):
+    """Pools whose length is not a multiple of 4 (read entry by entry), that
+    cross the one-block selection's 4096-entry load rows, fill all four, or
+    exceed them (the filter plan mapping pool entries)."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=21000, Di=128)
+    log(f"reindex pool sizes K_full={K_full} K2={K2}")
     _chain(GpuCache(wl), K_full, K2)
 
 

@@ -160,7 +160,8 @@ def test_paged_ragged_batch_and_workspace_reuse():
 
 
 @pytest.mark.parametrize("mode,K_full,K2", [("lognormal", 4096, 512), ("fine", 20000, 3000),
-                                             ("signed", 1000, 1000)])
+                                             ("signed", 1000, 1000), ("fine", 8191, 2000),
+                                             ("lognormal", 12290, 3000)])
 def test_reindex_scaled(mode, K_full, K2):
     """Full layer (scaled) builds the pool; a Reindex layer with its own
     query ranks the pool entries by their scaled values."""

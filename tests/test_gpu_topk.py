@@ -56,6 +56,17 @@ def test_short_contexts(L):
     _check(gc, gen.idx_query(wl), 16)
 
 
+@pytest.mark.parametrize("L", [4224, 4225, 12416, 16512, 16513])
+def test_one_block_row_boundaries(L):
+    """Candidate counts at the one-block selection's load-row edges: 4096
+    (one full row), 4097 (one live entry in the second), 12288, 16384 (the
+    largest one-block case, four full rows) and 16385 (the filter plan)."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=L)
+    log(f"topk row boundary L={L}")
+    gc = GpuCache(wl)
+    _check(gc, gen.idx_query(wl), 2048)
+
+
 def _tie_keys(mode):
     def fn(b, k):
         L = k.shape[0]
