@@ -88,6 +88,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// Inclusive running maximum over the 64 lanes of a wave of values >= 0 (the
+// same DPP steps as wave_inclusive_scan; a lane with no source keeps its own
+// value); lane 63 holds the wave's maximum.
+__device__ __forceinline__ int wave_inclusive_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return x;
+}
+
 // Given the NT/64 wave totals in `scratch` (after a barrier): the sum of the
 // totals of the waves before the calling one, and of all of them, both
 // wave-uniform.  Lane w < NT/64 reads total w; one wave scan and two lane

@@ -32,6 +32,7 @@ namespace csa2 {
 constexpr int kSelNT = 1024;                     // threads of the one-block-per-sequence kernels
 constexpr int kSelWaves = kSelNT / 64;
 constexpr int kListCap = 6144;                   // candidates the final kernel keeps in LDS
+constexpr int kDirectPer = 8;                    // slots per thread in the final kernel's direct gather
 constexpr int kFiltPer = 16;                     // entries per thread in the filter kernel
 constexpr int kFiltChunk = kBlock * kFiltPer;    // 4096 entries per filter block
 
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   __shared__ uint2 list[kListCap];
   __shared__ int scan_scratch[kSelWaves];
   __shared__ int2 wave_tot[kSelWaves];
-  __shared__ int sh[6];
+  __shared__ int sh[7];
   __shared__ uint32_t hist3[KT::kThree ? kBins : 1];
 
   const int b = blockIdx.x;
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   if (tid == 0) {                                // visible after find_digit_in's barriers
     sh[0] = top_t1;
     sh[1] = top_above1;
+    sh[6] = 0;                                   // the largest chunk count (general plan)
   }
   find_digit_in<kSelNT>(bins2, top_t1 >= 0 ? K - top_above1 : 1, scan_scratch, &sh[2], &sh[3]);
   {
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
     written = nsel < K ? nsel : K;
   } else {
     // ---- general: concatenate the slot lists (offsets first)
-    int total = 0;
+    int total = 0, vmax = 0;
     for (int c0 = 0; c0 < n_chunks; c0 += kSelNT) {
       const int c = c0 + tid;
       const int v = c < n_chunks ? (int)counts[c] : 0;
@@ -553,9 +555,17 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       const int pre = block_exclusive_scan<kSelNT>(v, scan_scratch, &round_total);
       if (c < n_chunks) offs[c] = total + pre;
       total += round_total;
+      vmax = v > vmax ? v : vmax;
     }
+    vmax = wave_inclusive_max(vmax);
+    if (lane == 63) atomicMax(&sh[6], vmax);
     if (tid == 0) offs[n_chunks] = total;
     __syncthreads();
+    // direct gather: a power-of-two group of tpc threads per chunk, each
+    // taking the chunk's slots j, j + tpc, .. (kDirectPer of them), when no
+    // chunk holds more than that
+    const int np2 = n_chunks > 1 ? 1 << (32 - __builtin_clz((unsigned)(n_chunks - 1))) : 1;
+    const int tpc = np2 <= kSelNT ? kSelNT / np2 : 0;
     if (n_chunks <= 2 * kSelWaves) {
       // few chunks: each wave walks whole chunks, its lanes over consecutive
       // candidates
@@ -564,25 +574,58 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
         for (int i = lane; i < cnt && o + i < kListCap; i += 64)
           list[o + i] = cand_row[(size_t)c * kFiltChunk + i];
       }
+    } else if (tpc > 0 && sh[6] <= tpc * kDirectPer) {
+      const int c = tid / tpc, j = tid % tpc;
+      if (c < n_chunks) {
+        const int o = offs[c], cn = offs[c + 1] - o;
+        uint2 v[kDirectPer];
+#pragma unroll
+        for (int m = 0; m < kDirectPer; ++m) {
+          const int i = j + tpc * m;
+          v[m] = cand_row[i < cn ? (size_t)c * kFiltChunk + i : 0];
+        }
+#pragma unroll
+        for (int m = 0; m < kDirectPer; ++m) {
+          const int i = j + tpc * m;
+          if (i < cn && o + i < kListCap) list[o + i] = v[m];
+        }
+      }
     } else {
       // many small chunks: list slot f (< kListCap) comes from the chunk c
-      // with offs[c] <= f < offs[c + 1], found by a fixed 12-step bisection
-      // over the offsets (unrolled, so a thread's searches interleave); its
-      // slots are independent, so their loads are in flight together
-      // instead of one chunk after another
+      // with offs[c] <= f < offs[c + 1], the largest c whose offset is at
+      // most f, found by binary lifting over the offsets.  A thread's kPer
+      // searches go step by step together (their LDS reads issued at once,
+      // one wait per step), then every slot's load is issued at once
+      // (clamped addresses, no branches), instead of one search and one
+      // chunk after another
       constexpr int kPer = (kListCap + kSelNT - 1) / kSelNT;
       const int lim = total < kListCap ? total : kListCap;
+      int c[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) c[q] = 0;            // offs[0] = 0 <= f
+      // steps top, top/2, .., 1 reach any chunk below n_chunks
+      const int top = n_chunks > 1 ? 1 << (31 - __builtin_clz((unsigned)(n_chunks - 1))) : 0;
+      for (int step = top; step > 0; step >>= 1) {
+        int o[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int cand = c[q] + step;
+          o[q] = offs[cand < n_chunks ? cand : n_chunks];
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int cand = c[q] + step;
+          c[q] = (cand < n_chunks && o[q] <= tid + q * kSelNT) ? cand : c[q];
+        }
+      }
+      int ofs[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) ofs[q] = offs[c[q]];
       uint2 v[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int f = tid + q * kSelNT;
-        int c = 0;                                  // offs[0] = 0 <= f
-#pragma unroll
-        for (int step = kMaxSelChunks / 2; step > 0; step >>= 1) {
-          const int cand = c + step;                // at most kMaxSelChunks - 1
-          c = (cand < n_chunks && offs[cand] <= f) ? cand : c;
-        }
-        v[q] = f < lim ? cand_row[(size_t)c * kFiltChunk + (f - offs[c])] : make_uint2(0u, 0u);
+        v[q] = cand_row[f < lim ? (size_t)c[q] * kFiltChunk + (f - ofs[q]) : 0];
       }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {

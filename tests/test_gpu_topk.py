@@ -151,6 +151,24 @@ def test_clustered_top_scores():
         _check(gc, q, K)
 
 
+def test_final_gather_plans():
+    """300K candidates (73 filter chunks): with spread-out top scores every
+    chunk's kept list fits its group of 8 gathering threads (the direct
+    gather); with the top scores packed into two 1024-position blocks, or a
+    K that keeps hundreds per chunk, a chunk overflows its group and the
+    slot-by-slot search over the chunk offsets runs instead."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=300_000, Di=64)
+    q = gen.idx_query(wl)
+    log("topk L=300000 spread")
+    gc = GpuCache(wl, keep_kv=False)
+    for K in (2048, 9000):
+        _check(gc, q, K)
+    del gc
+    log("topk L=300000 clustered")
+    gc = GpuCache(wl, keep_kv=False, keys_fn=_clustered_keys(q, [40 * 1024, 200 * 1024]))
+    _check(gc, q, 2048)
+
+
 def test_deterministic_and_workspace_reuse():
     """Same call twice on one workspace (the first leaves its control words
     zero) and on a fresh one: identical bits; a shorter max_ctx bound too."""
