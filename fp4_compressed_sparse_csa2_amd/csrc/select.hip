@@ -339,15 +339,18 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
   const int32_t* row = a.scores + (size_t)b * a.stride;
   uint32_t* ctrl = a.hist1 + (size_t)b * kCtrlWords;
 
-  // this thread's 16 scores and the block's share of the histogram, loaded together
+  // the block's share of the histogram, then this thread's 16 scores, all in
+  // flight together: the score loads are unconditional (a thread past n
+  // reads the row's first 16 entries, inside the row, and keeps none), so
+  // that no branch holds them and their use
+  const DigitBins<kBlock> bins = load_digit_bins<kBlock, kHistReps>(ctrl);
   const int p0 = chunk0 + (int)threadIdx.x * kFiltPer;
   uint4 sv[kFiltPer / 4];
-  if (p0 < n) {
-    const uint4* src = reinterpret_cast<const uint4*>(row + p0);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(row + (p0 < n ? p0 : 0));
 #pragma unroll
     for (int i = 0; i < kFiltPer / 4; ++i) sv[i] = src[i];
   }
-  const DigitBins<kBlock> bins = load_digit_bins<kBlock, kHistReps>(ctrl);
   find_digit_in<kBlock>(bins, a.K, scan_scratch, &sh_t1, &sh_above1);
   const uint32_t t1 = (uint32_t)sh_t1;
   if (chunk == 0 && threadIdx.x == 0) {  // for the final stage (every block finds the same)
