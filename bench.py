@@ -928,16 +928,16 @@ TRACE_STEPS = [
     ("b8_64k step: csa2_append_index_topk + csa2_sparse_decode",
      [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode_kernel<512, 16, true>",
-      r"sparse_combine_kernel<512, 16>"], 9),
+      r"sparse_combine_kernel<512, 16, \d+>"], 9),
     ("b1_1m step: csa2_append_index_topk + csa2_sparse_decode",
      [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode\w*_kernel<512[^>]*>",
-      r"sparse_combine_kernel<512, \d+>"], 2),
+      r"sparse_combine_kernel<512, \d+, \d+>"], 2),
     ("b128_rag csa2_index_topk",
      [r"index_score_kernel<128, false>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>"], 128),
     ("b128_rag csa2_sparse_decode",
-     [r"sparse_decode64_kernel<512>", r"sparse_combine_kernel<512, 64>"], None),
+     [r"sparse_decode64_kernel<512>", r"sparse_combine_kernel<512, 64, \d+>"], None),
     ("b8_64k csa2_reindex 8192 -> 2048",
      [r"reindex_score_kernel<128, false>", r"select_single_kernel<IntKeys, true>"], None),
 ]

@@ -1107,16 +1107,18 @@ __global__ __launch_bounds__(kBlock8, 1) void sparse_decode64_kernel(
   }
 }
 
-// LSE merge of the split partials.  Block = (unit, HPB heads); thread = one
-// float4 of one head's output; every load of a batch of 16 splits is issued
-// before any is used.
-template <int D, int HG>
+// LSE merge of the split partials.  Block = (unit, HPB heads); thread = V
+// float4s of one head's output (T4 float4s apart); every load of a batch of
+// SB splits is issued before any is used.  V > 1 for few splits, so that a
+// thread still has several loads in flight and the grid fits the chip at once.
+template <int D, int HG, int V>
 __global__ __launch_bounds__(kBlock) void sparse_combine_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml, int H, int n_splits,
     float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int T4 = D / 4;                 // threads per head
+  constexpr int T4 = D / 4 / V;             // threads per head
   constexpr int HPB = kBlock / T4;          // heads per block
-  constexpr int SB = 16;                    // splits per batch of loads
+  constexpr int SB = 16 / V;                // splits per batch of loads
+  static_assert(HPB <= HG && HG % HPB == 0, "a block's heads lie in one head group");
   const int n_hg = H / HG;
   const int unit = blockIdx.x / (HG / HPB);
   const int h = (blockIdx.x % (HG / HPB)) * HPB + (int)threadIdx.x / T4;
@@ -1127,20 +1129,27 @@ __global__ __launch_bounds__(kBlock) void sparse_combine_kernel(
   const float4* src = reinterpret_cast<const float4*>(part_o + (ubase * HG + h) * D) + d4;
 
   float M = -INFINITY, Lsum = 0.f;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 a[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) a[v] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < n_splits; s0 += SB) {
     float2 ml[SB];
-    float4 x[SB];
+    float4 x[SB][V];
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       if (s0 + i < n_splits) {
         ml[i] = part_ml[(ubase + s0 + i) * HG + h];
-        const floatx4 t =       // partials are read once: non-temporal
-            __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + (s0 + i) * ostep));
-        x[i] = make_float4(t.x, t.y, t.z, t.w);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const floatx4 t =     // partials are read once: non-temporal
+              __builtin_nontemporal_load(
+                  reinterpret_cast<const floatx4*>(src + (s0 + i) * ostep + v * T4));
+          x[i][v] = make_float4(t.x, t.y, t.z, t.w);
+        }
       } else {
         ml[i] = make_float2(-INFINITY, 0.f);
-        x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[i][v] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     float mb = M;
@@ -1150,24 +1159,33 @@ __global__ __launch_bounds__(kBlock) void sparse_combine_kernel(
     if (mb == -INFINITY) continue;                      // nothing with weight yet
     const float r = M == -INFINITY ? 0.f : exp2f(M - mb);
     Lsum *= r;
-    a.x *= r;
-    a.y *= r;
-    a.z *= r;
-    a.w *= r;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      a[v].x *= r;
+      a[v].y *= r;
+      a[v].z *= r;
+      a[v].w *= r;
+    }
     M = mb;
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       const float w = ml[i].y > 0.f ? exp2f(ml[i].x - M) : 0.f;
       Lsum += w * ml[i].y;
-      a.x += w * x[i].x;
-      a.y += w * x[i].y;
-      a.z += w * x[i].z;
-      a.w += w * x[i].w;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        a[v].x += w * x[i][v].x;
+        a[v].y += w * x[i][v].y;
+        a[v].z += w * x[i][v].z;
+        a[v].w += w * x[i][v].w;
+      }
     }
   }
   const float il = Lsum > 0.f ? 1.0f / Lsum : 0.0f;
   const size_t orow = (size_t)b * H + hg * HG + h;
-  reinterpret_cast<float4*>(out + orow * D)[d4] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    reinterpret_cast<float4*>(out + orow * D)[d4 + v * T4] =
+        make_float4(a[v].x * il, a[v].y * il, a[v].z * il, a[v].w * il);
   if (d4 == 0 && lse != nullptr) lse[orow] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
@@ -1286,10 +1304,20 @@ static void launch_decode_hg(const CacheArgs& c, const DecodePlan& pl, const int
                        pl.n_splits, pl.split_tiles, pl.win_sep);
   }
   if (pl.n_splits > 1) {
-    constexpr int HPB = kBlock / (D / 4);
-    hipLaunchKernelGGL((sparse_combine_kernel<D, HG>), dim3(units * (HG / HPB)), dim3(kBlock), 0,
-                       st, reinterpret_cast<const float*>(ws + w.part_o),
-                       reinterpret_cast<const float2*>(ws + w.part_ml), H, pl.n_splits, out, lse);
+    // few splits: four float4s per thread (two where a block of four would
+    // span more than one head group)
+    constexpr int VF = kBlock * 16 / D <= HG ? 4 : 2;
+    const float* po = reinterpret_cast<const float*>(ws + w.part_o);
+    const float2* pm = reinterpret_cast<const float2*>(ws + w.part_ml);
+    if (pl.n_splits <= 4) {
+      constexpr int HPB = kBlock * VF * 4 / D;
+      hipLaunchKernelGGL((sparse_combine_kernel<D, HG, VF>), dim3(units * (HG / HPB)),
+                         dim3(kBlock), 0, st, po, pm, H, pl.n_splits, out, lse);
+    } else {
+      constexpr int HPB = kBlock * 4 / D;
+      hipLaunchKernelGGL((sparse_combine_kernel<D, HG, 1>), dim3(units * (HG / HPB)),
+                         dim3(kBlock), 0, st, po, pm, H, pl.n_splits, out, lse);
+    }
   }
 }
 

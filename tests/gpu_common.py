@@ -117,6 +117,8 @@ DECODE_PLANS = {
     "hg64_split3": ("64", "3"),
     "hg64_split1": ("64", "1"),
     "hg16_split2": ("16", "2"),
+    "hg16_split4": ("16", "4"),
+    "hg64_split5": ("64", "5"),
 }
 
 

@@ -70,10 +70,10 @@ def test_trace_summary_finds_each_step(tmp_path):
         k("select_filter_kernel<csa2::IntKeys>", 5000)
         k("select_final_kernel<4, csa2::IntKeys, false>", 6000)
         k("sparse_decode_kernel<512, 16, true>", 13000, gap_ns=gap)
-        k("sparse_combine_kernel<512, 16>", 5000)
+        k("sparse_combine_kernel<512, 16, 1>", 5000)
         k("fill_zero_kernel", 2000)
     k("sparse_decode64_kernel<512>", 70000)
-    k("sparse_combine_kernel<512, 64>", 15000)
+    k("sparse_combine_kernel<512, 64, 4>", 15000)
     path = tmp_path / "trace.csv"
     path.write_text(hdr + "\n" + "\n".join(rows) + "\n")
     out = bench.trace_summary(str(path))

@@ -143,9 +143,11 @@ def test_large_batch_sharp(q_std, mult, plan):
     _decode_and_check(GpuCache(wl), 2048, plan=plan)
 
 
-@pytest.mark.parametrize("plan", ["auto", "hg64"])
+@pytest.mark.parametrize("plan", ["auto", "hg64", "hg16_split4", "hg64_split5"])
 @pytest.mark.parametrize("D,H", [(256, 32), (128, 128), (256, 64)])
 def test_other_widths(D, H, plan):
+    """Latent widths 256 and 128; with 4 splits of 16-head blocks or 2 of
+    64-head ones the combine takes several float4s per thread."""
     wl = gen.WORKLOADS["tiny"].with_(B=2, L=2000, D=D, H=H, Di=128)
     log(f"decode D={D} H={H} plan={plan}")
     _decode_and_check(GpuCache(wl), 512, plan=plan)
