@@ -55,6 +55,14 @@ def test_chain_pool_sizes(K_full, K2):
     _chain(GpuCache(wl), K_full, K2)
 
 
+def test_page_table_past_lds_stage():
+    """A 70K-token context (1094 pages): the scoring kernel reads the page
+    table from global memory instead of its 1024-entry LDS copy."""
+    wl = gen.WORKLOADS["tiny"].with_(B=2, L=70_000, Di=64)
+    log("reindex 70K context (page table past the LDS stage)")
+    _chain(GpuCache(wl, keep_kv=False), 3000, 1000)
+
+
 def test_short_pools():
     """Contexts of 0..900 tokens: pools shorter than K', padded with -1."""
     wl = gen.WORKLOADS["b128_rag"].with_(B=12, L=900, L_min=0, D=128, H=16, Di=64)
