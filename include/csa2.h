@@ -475,8 +475,8 @@ int csa2_reindex_scaled(const csa2_cache* cache, const int8_t* q_idx, const floa
 
 /*
  * csa2_stream_read -- a measurement aid, not a step of the method: reads
- * `bytes` of device memory at src once with 16-byte non-temporal loads and
- * XORs every word into *sink (device uint32; its old value is kept, so the
+ * `bytes` of device memory at src once with 16-byte non-temporal loads (each
+ * workgroup one contiguous 16 KB run) and XORs every word into *sink (device uint32; its old value is kept, so the
  * result is defined but of no use beyond keeping the loads).  Timing it
  * beside the method's calls gives the rate a plain read-only kernel reaches
  * on this memory, the reference against which the calls' achieved rates are
