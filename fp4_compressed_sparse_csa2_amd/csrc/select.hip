@@ -112,7 +112,7 @@ static_assert(kRegRow <= 0xFFFF, "a row prefix fits a packed half");
 template <typename KT, bool POOL>
 __global__ __launch_bounds__(kSingleNT) void select_single_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[kBins];
-  __shared__ int32_t pool_lds[POOL ? kSingleMax : 1];   // the sequence's pool row
+  __shared__ __attribute__((aligned(16))) int32_t pool_lds[POOL ? kSingleMax : 1];   // pool row
   __shared__ int scan_scratch[kSingleWaves];
   __shared__ int row_scan[kRegRows][kSingleWaves];
   __shared__ int sh_t1, sh_above1, sh_t2, sh_above2, sh_t3, sh_above3;

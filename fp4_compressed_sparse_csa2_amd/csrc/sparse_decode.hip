@@ -274,66 +274,24 @@ __global__ __launch_bounds__(kBlock, HG == 16 ? 2 : 1) void sparse_decode_kernel
     }
   }
 
-  // ---- queries, staged once per block: per round, wave w converts 4 heads
-  // (16 lanes per head) to exact f16 copies of q * 2^e, e chosen per head so
-  // that the largest |q| lands in [2^14, 2^15); the staging aliases X
-  _Float16* Qs = X;
+  // ---- queries: every load issued now; converted (below) once the rows of
+  // the first FP4 tile are requested
+  uint4 qraw[HB][QPL];
 #pragma unroll
   for (int round = 0; round < HB; ++round) {
     const int hq = round * 16 + wave * 4 + lg;           // head within the group
     const uint16_t* src = q + ((size_t)b * H + hg * HG + hq) * D + lc * (D / 16);
-    uint4 qraw[QPL];
-    uint32_t qmax = 0;
 #pragma unroll
-    for (int i = 0; i < QPL; ++i) {
-      qraw[i] = reinterpret_cast<const uint4*>(src)[i];
-      const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qmax = max(qmax, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, m, 16));
-    int qexp = 0;
-    if (qmax != 0u) {
-      int ex;
-      frexpf(bf16_to_f32(qmax), &ex);     // max|q| in [2^(ex-1), 2^ex)
-      qexp = 15 - ex;
-    }
-    if (lc == 0) q_exp[hq] = qexp;
-    _Float16* dst = Qs + hq * QS + lc * (D / 16);
-#pragma unroll
-    for (int i = 0; i < QPL; ++i) {
-      const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-      half8 h;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        h[2 * k] = (_Float16)ldexpf(bf16_to_f32(w[k] & 0xFFFFu), qexp);
-        h[2 * k + 1] = (_Float16)ldexpf(bf16_to_f32(w[k] >> 16), qexp);
-      }
-      *reinterpret_cast<half8*>(dst + 8 * i) = h;
-    }
+    for (int i = 0; i < QPL; ++i) qraw[round][i] = reinterpret_cast<const uint4*>(src)[i];
   }
-  if (PTC && fa < fb0) {
+  if (PTC) {
+    if (fa < fb0) {
 #pragma unroll
-    for (int i = 0; i < kPtCache / kBlock; ++i)
-      if (i * kBlock < max_pages) pt_lds[i * kBlock + tid] = ptv[i];
+      for (int i = 0; i < kPtCache / kBlock; ++i)
+        if (i * kBlock < max_pages) pt_lds[i * kBlock + tid] = ptv[i];
+    }
+    __syncthreads();                    // the page table is in LDS
   }
-  __syncthreads();
-  // QK operands.  The contraction over D may visit the channels in any order
-  // as long as X and Q agree: k-step kk takes, in lane row lg, channels
-  // lg*D/4 + 8kk .. +8, which are exactly the channels a gather lane holds,
-  // so the X operand comes straight from the dequantised registers.
-  // qf[hb][kk]: head 16hb + lc, channels lg*D/4 + 8kk .. +8.
-  half8 qf[HB][KQ];
-  float scale2[HB];                       // logits in log2 units: scale2 * (q~ . x)
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-    for (int kk = 0; kk < KQ; ++kk)
-      qf[hb][kk] = *reinterpret_cast<const half8*>(Qs + (hb * 16 + lc) * QS + lg * DQ + 8 * kk);
-    scale2[hb] = ldexpf(scale, -q_exp[hb * 16 + lc]) * kLog2e;
-  }
-  __syncthreads();                      // the staging area becomes the X tile
 
   const int L = L_raw < 0 ? 0 : (L_raw > max_pages * kPage ? max_pages * kPage : L_raw);
   const int n_glob = L > kWindow ? L - kWindow : 0;     // selectable positions
@@ -355,19 +313,71 @@ __global__ __launch_bounds__(kBlock, HG == 16 ? 2 : 1) void sparse_decode_kernel
   auto rowkey_of = [&](int p, int pg) -> long long {
     return (p >= 0 && pg >= 0 && pg < num_pages) ? ((long long)pg << 6) | (p & (kPage - 1)) : -1;
   };
-  int pg2 = -1;
-  long long rk0 = -1, rk1 = -1;
+  // the first FP4 tile's rows, requested unconditionally (a block with no
+  // FP4 tile loads row 0 of page 0 and never uses it), so that no branch
+  // makes the query conversion below wait for them
+  p0 = pos_ok(fa) ? p0 : -1;
+  p1 = pos_ok(fa + 1) ? p1 : -1;
+  p2 = pos_ok(fa + 2) ? p2 : -1;
+  int pg2 = page_of(p2);
+  long long rk0 = rowkey_of(p0, page_of(p0)), rk1 = rowkey_of(p1, page_of(p1));
   RowPart<D> cur, nxt;
-  if (fa < fb) {
-    p0 = pos_ok(fa) ? p0 : -1;
-    p1 = pos_ok(fa + 1) ? p1 : -1;
-    p2 = pos_ok(fa + 2) ? p2 : -1;
-    const int pg0 = page_of(p0), pg1 = page_of(p1);
-    pg2 = page_of(p2);
-    rk0 = rowkey_of(p0, pg0);
-    rk1 = rowkey_of(p1, pg1);
-    load_row_part<D>(cur, pages, rk0, page_bytes, lg);
+  load_row_part<D>(cur, pages, rk0, page_bytes, lg);
+
+  // queries, staged once per block: per round, wave w converts 4 heads (16
+  // lanes per head) to exact f16 copies of q * 2^e, e chosen per head so
+  // that the largest |q| lands in [2^14, 2^15); the staging aliases X
+  _Float16* Qs = X;
+#pragma unroll
+  for (int round = 0; round < HB; ++round) {
+    const int hq = round * 16 + wave * 4 + lg;           // head within the group
+    uint32_t qmax = 0;
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const uint32_t w[4] = {qraw[round][i].x, qraw[round][i].y, qraw[round][i].z,
+                             qraw[round][i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qmax = max(qmax, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, m, 16));
+    int qexp = 0;
+    if (qmax != 0u) {
+      int ex;
+      frexpf(bf16_to_f32(qmax), &ex);     // max|q| in [2^(ex-1), 2^ex)
+      qexp = 15 - ex;
+    }
+    if (lc == 0) q_exp[hq] = qexp;
+    _Float16* dst = Qs + hq * QS + lc * (D / 16);
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) {
+      const uint32_t w[4] = {qraw[round][i].x, qraw[round][i].y, qraw[round][i].z,
+                             qraw[round][i].w};
+      half8 h;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[2 * k] = (_Float16)ldexpf(bf16_to_f32(w[k] & 0xFFFFu), qexp);
+        h[2 * k + 1] = (_Float16)ldexpf(bf16_to_f32(w[k] >> 16), qexp);
+      }
+      *reinterpret_cast<half8*>(dst + 8 * i) = h;
+    }
   }
+  __syncthreads();
+  // QK operands.  The contraction over D may visit the channels in any order
+  // as long as X and Q agree: k-step kk takes, in lane row lg, channels
+  // lg*D/4 + 8kk .. +8, which are exactly the channels a gather lane holds,
+  // so the X operand comes straight from the dequantised registers.
+  // qf[hb][kk]: head 16hb + lc, channels lg*D/4 + 8kk .. +8.
+  half8 qf[HB][KQ];
+  float scale2[HB];                       // logits in log2 units: scale2 * (q~ . x)
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk)
+      qf[hb][kk] = *reinterpret_cast<const half8*>(Qs + (hb * 16 + lc) * QS + lg * DQ + 8 * kk);
+    scale2[hb] = ldexpf(scale, -q_exp[hb * 16 + lc]) * kLog2e;
+  }
+  __syncthreads();                      // the staging area becomes the X tile
 
   // running softmax state of head 16hb + lc (every lane of the head holds
   // the same); acc[hb][nb] holds O^T[dims wave*DQ + 16nb + 4lg + i][head 16hb + lc]
