@@ -401,6 +401,7 @@ __global__ __launch_bounds__(kBlock) void select_filter_kernel(SelectArgs a) {
 template <int SPL, typename KT, bool POOL>
 __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
   constexpr int spl = SPL;
+  static_assert(kSelWaves * 64 * SPL <= 0xFFFF, "direct-plan counts fit a packed half");
   __shared__ int offs[kMaxSelChunks + 1];
   __shared__ uint2 list[kListCap];
   __shared__ int scan_scratch[kSelWaves];
@@ -523,17 +524,14 @@ __global__ __launch_bounds__(kSelNT) void select_final_kernel(SelectArgs a) {
       gw += (int)__popcll(bg) << bit;
       tw += (int)__popcll(bt) << bit;
     }
-    if (lane == 0) wave_tot[wave] = make_int2(gw, tw);
+    // the waves' counts packed as above + (ties << 16) (at most 16 x 64 x
+    // SPL = 16384 each), summed by DPP; scan_scratch's last reader passed a
+    // barrier above
+    if (lane == 0) scan_scratch[wave] = gw + (tw << 16);
     __syncthreads();
-    int g = gpre, t = tpre, G = 0, T = 0;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int2 v = wave_tot[w];
-      g += w < wave ? v.x : 0;
-      t += w < wave ? v.y : 0;
-      G += v.x;
-      T += v.y;
-    }
+    const int2 bt = waves_before_and_total<kSelNT>(scan_scratch);
+    int g = gpre + (bt.x & 0xFFFF), t = tpre + (bt.x >> 16);
+    const int G = bt.y & 0xFFFF, T = bt.y >> 16;
 #pragma unroll
     for (int k = 0; k < spl; ++k) {
       if ((gtm >> k) & 1u) {
