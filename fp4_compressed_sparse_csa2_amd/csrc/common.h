@@ -116,6 +116,22 @@ __device__ __forceinline__ int2 waves_before_and_total(const int* scratch) {
   return make_int2(before, __builtin_amdgcn_readlane(x, NW - 1));
 }
 
+// The same for two totals per wave (`tot`: NT/64 int2 after a barrier):
+// {before.x, before.y, total.x, total.y}, wave-uniform.
+template <int NT>
+__device__ __forceinline__ int4 waves_before_and_total2(const int2* tot) {
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 64, "one total per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int2 v = lane < NW ? tot[lane] : make_int2(0, 0);
+  const int x = wave_inclusive_scan(v.x), y = wave_inclusive_scan(v.y);
+  const int bx = wave == 0 ? 0 : __builtin_amdgcn_readlane(x, wave - 1);
+  const int by = wave == 0 ? 0 : __builtin_amdgcn_readlane(y, wave - 1);
+  return make_int4(bx, by, __builtin_amdgcn_readlane(x, NW - 1),
+                   __builtin_amdgcn_readlane(y, NW - 1));
+}
+
 // Exclusive prefix sum over an NT-thread block; returns the prefix, sets *total.
 // `scratch` must hold NT/64 ints of shared memory.  Contains barriers: every
 // thread of the block must call it.  SYNC_AFTER = false leaves out the

@@ -155,7 +155,6 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 template <int NT, typename Get, typename Put>
 __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, int K,
                              int2* wave_tot, Put put) {
-  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int run = ((total + NT - 1) / NT) * 64;          // a multiple of 64 per wave
   const int f0 = wave * run;
@@ -169,15 +168,9 @@ __device__ int emit_in_order(Get get, int total, uint32_t tau, int need_ties, in
   }
   if (lane == 0) wave_tot[wave] = make_int2(g, t);
   __syncthreads();
-  int g0 = 0, t0 = 0, G = 0, T = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int2 v = wave_tot[w];
-    g0 += w < wave ? v.x : 0;
-    t0 += w < wave ? v.y : 0;
-    G += v.x;
-    T += v.y;
-  }
+  const int4 bt = waves_before_and_total2<NT>(wave_tot);
+  int g0 = bt.x, t0 = bt.y;
+  const int G = bt.z, T = bt.w;
   for (int f = f0 + lane; f - lane < f1; f += 64) {
     const bool live = f < f1;
     const uint2 c = live ? get(f) : make_uint2(0u, 0u);
