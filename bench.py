@@ -932,15 +932,15 @@ def traffic_from(fetch_dir: str, write_dir: str, steps: int) -> dict:
 # (title, kernel-name patterns in launch order, grid rows of the first kernel).
 TRACE_STEPS = [
     ("b8_64k step: csa2_append_index_topk + csa2_sparse_decode",
-     [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
+     [r"append_score_kernel<512, 128, \d+>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode_kernel<512, 16, true>",
       r"sparse_combine_kernel<512, 16, \d+>"], 9),
     ("b1_1m step: csa2_append_index_topk + csa2_sparse_decode",
-     [r"append_score_kernel<512, 128>", r"select_filter_kernel<IntKeys>",
+     [r"append_score_kernel<512, 128, \d+>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>", r"sparse_decode\w*_kernel<512[^>]*>",
       r"sparse_combine_kernel<512, \d+, \d+>"], 2),
     ("b128_rag csa2_index_topk",
-     [r"index_score_kernel<128, false>", r"select_filter_kernel<IntKeys>",
+     [r"index_score_kernel<128, false, \d+>", r"select_filter_kernel<IntKeys>",
       r"select_final_kernel<\d+, IntKeys, false>"], 128),
     ("b128_rag csa2_sparse_decode",
      [r"sparse_decode64_kernel<512>", r"sparse_combine_kernel<512, 64, \d+>"], None),

@@ -66,7 +66,7 @@ def test_trace_summary_finds_each_step(tmp_path):
         t += dur_ns
 
     for gap in (0, 1000):
-        k("append_score_kernel<512, 128>", 13000, grid_y=9)
+        k("append_score_kernel<512, 128, 16>", 13000, grid_y=9)
         k("select_filter_kernel<csa2::IntKeys>", 5000)
         k("select_final_kernel<4, csa2::IntKeys, false>", 6000)
         k("sparse_decode_kernel<512, 16, true>", 13000, gap_ns=gap)

@@ -87,6 +87,14 @@ def test_paged_ragged_d512():
     _run_pair(GpuCache(wl, keep_kv=False), 1, 2048, True)
 
 
+def test_many_block_scoring_grid():
+    """The fused call on a grid of 8-page scoring blocks (40 sequences of
+    100K-110K positions)."""
+    wl = gen.WORKLOADS["b128_rag"].with_(B=40, L=110_000, L_min=100_000, D=128, H=16)
+    log("fused append+topk many-block scoring grid")
+    _run_pair(GpuCache(wl, keep_kv=False), 1, 2048, True)
+
+
 def test_b8_64k_shape():
     wl = gen.WORKLOADS["b8_64k"].with_(append_steps=1)
     log("fused append+topk b8_64k")

@@ -186,6 +186,17 @@ def test_reindex_scaled(mode, K_full, K2):
         assert int(cnt[b]) == wcnt and np.array_equal(idx[b], want), f"b={b}"
 
 
+@pytest.mark.parametrize("Di", [64, 128])
+def test_many_block_scoring_grid(Di):
+    """Scaled keys on a grid of 8-page scoring blocks (40 sequences of
+    100K-110K positions)."""
+    wl = gen.WORKLOADS["b128_rag"].with_(B=40, L=110_000, L_min=100_000, D=128, H=16, Di=Di)
+    log(f"scaled many-block scoring grid Di={Di}")
+    gc = GpuCache(wl, keep_kv=False)
+    ks, scales = _store_scales(gc, "lognormal")
+    _check_topk(gc, gen.idx_query(wl), ks, scales, 2048)
+
+
 def test_e4m3_scales():
     """E4M3 scale bytes: stored as their exact fp32 values, then ranked."""
     wl = gen.WORKLOADS["b128_rag"].with_(B=6, L=30000, L_min=1, D=128, H=16, Di=64)

@@ -169,6 +169,16 @@ def test_final_gather_plans():
     _check(gc, q, 2048)
 
 
+@pytest.mark.parametrize("Di", [64, 128])
+def test_many_block_scoring_grid(Di):
+    """40 sequences of up to 110K positions: at least 4096 scoring blocks of
+    16 pages, so the scoring launch runs 8-page blocks."""
+    wl = gen.WORKLOADS["b128_rag"].with_(B=40, L=110_000, L_min=100_000, D=128, H=16, Di=Di)
+    log(f"topk many-block scoring grid Di={Di}")
+    gc = GpuCache(wl, keep_kv=False)
+    _check(gc, gen.idx_query(wl), 2048)
+
+
 def test_deterministic_and_workspace_reuse():
     """Same call twice on one workspace (the first leaves its control words
     zero) and on a fresh one: identical bits; a shorter max_ctx bound too."""
