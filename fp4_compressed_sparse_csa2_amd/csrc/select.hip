@@ -191,6 +191,13 @@ __global__ __launch_bounds__(kSingleNT) void select_single_kernel(SelectArgs a) 
   find_digit_in<kSingleNT>(bins, K, scan_scratch, &sh_t1, &sh_above1);
   const bool have_t1 = sh_t1 >= 0;
   const uint32_t t1 = (uint32_t)sh_t1;
+  {
+    // every thread has read its bins (before find_digit_in's barriers):
+    // return the histogram replicas to zero for the next call now, so that
+    // the stores drain while the entries are classified
+    uint4* h4 = reinterpret_cast<uint4*>(h1);
+    for (int i = tid; i < kCtrlHist2 / 4; i += kSingleNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // keys of the held entries (rows past n are skipped, block-uniformly) and
   // 4-bit masks of the live ones, and of those whose top digit is t1
@@ -318,8 +325,6 @@ __global__ __launch_bounds__(kSingleNT) void select_single_kernel(SelectArgs a) 
     if (a.out_sel_scores != nullptr) a.out_sel_scores[(size_t)b * K + j] = 0;
   }
   if (tid == 0) a.out_count[b] = written;
-  uint4* h4 = reinterpret_cast<uint4*>(h1);     // the histogram replicas, for the next call
-  for (int i = tid; i < kCtrlHist2 / 4; i += kSingleNT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------------ filter
